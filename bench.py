@@ -1,0 +1,288 @@
+#!/usr/bin/env python3
+"""Benchmark of the one-shot Lamport-mailbox logits gather on one MI355X.
+
+Prints ONE JSON line. The timed step is one decode gather -- TP=8 virtual
+ranks, V=163840, M=1 row, mailbox cap 8 -- issued K times back to back on one
+stream with every input already resident in HBM (8 input sets cycled, K
+distinct outputs); ``value`` is microseconds per gather from HIP events around
+the K calls. The same run measures the M=256 gather (the bandwidth half of the
+metric) on three rotating buffer sets, so each call's inputs were evicted from
+the 256 MB Infinity Cache by the two calls before it, and reports its
+algorithmic bandwidth against the 8 TB/s HBM peak in ``roofline``. The CPU
+oracle is timed on a bounded sample of the same inputs (``cpu_baseline``) and
+its results double as the check of the GPU outputs; a mismatch aborts the run.
+
+Algorithmic bytes per gather: 5 * M * V * 2 (shard read, mailbox push write,
+mailbox poll read, output write, re-arm write).
+
+Modes: default (the JSON line); ``--pmc-probe`` runs only a plain 256 MiB copy
+and the M=256 fused gather a few times, for ``rocprofv3 --pmc`` counter runs.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "µs per logits gather at M=1 (V=163840, TP=8) + achieved HBM GB/s at M=256"
+HBM_PEAK_GBPS = 8000.0
+KERNEL_SOURCE = os.path.join(ROOT, "tp_vocab_logits_amd", "csrc", "hg_kernels.hip")
+COUNTERS = os.path.join(ROOT, "profiles", "fused_gather_m256_counters.json")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000, help="timed M=1 gathers")
+    ap.add_argument("--warmup", type=int, default=100, help="untimed M=1 gathers first")
+    ap.add_argument("--large-steps", type=int, default=60, help="timed M=256 gathers")
+    ap.add_argument("--variant", choices=["fused", "split"], default="fused")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--pmc-probe", action="store_true")
+    return ap.parse_args()
+
+
+class Timer:
+    """HIP events on the stream the kernels are launched on."""
+
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+
+    def __enter__(self):
+        self.torch.cuda.synchronize()
+        self.t0 = self.torch.cuda.Event(enable_timing=True)
+        self.t1 = self.torch.cuda.Event(enable_timing=True)
+        self.t0.record(self.stream)
+        return self
+
+    def __exit__(self, *exc):
+        self.t1.record(self.stream)
+        self.t1.synchronize()
+        self.torch.cuda.synchronize()
+        self.ms = self.t0.elapsed_time(self.t1)
+
+
+def main() -> int:
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": f"--gpus {args.gpus}: this benchmark runs on one GPU only; "
+                          "the TP ranks are virtual ranks inside that GPU"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    from tp_vocab_logits_amd import _lib
+    from tp_vocab_logits_amd import synthetic as syn
+    from tp_vocab_logits_amd.head_gather import HeadGather
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 3
+    lib = _lib.lib()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    sh = ctypes.c_void_p(stream.cuda_stream)
+
+    def call_fn(hg, variant):
+        h = hg.handle
+        if variant == "fused":
+            g = lib.hg_gather
+            return lambda ptrs, m, out: g(h, ptrs, m, out, sh)
+        push, collect = lib.hg_push, lib.hg_collect
+
+        def split(ptrs, m, out):
+            rc = push(h, ptrs, m, sh)
+            return rc if rc else collect(h, m, out, sh)
+        return split
+
+    # ---------------- M=256 inputs (three rotation sets) --------------------
+    wl = syn.WORKLOADS["fused"]
+    big_sets = []
+    for k in range(3):
+        b = syn.shard_set(wl, k)
+        syn.inject_sentinel_words(b, 0.001, 9000 + k)
+        big_sets.append(b)
+    big_dev = [syn.to_torch_bf16(b, dev) for b in big_sets]
+    big_out = [torch.empty((wl.rows, wl.vocab), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    big_ptrs = [_lib.pointer_array([t[r].data_ptr() for r in range(wl.tp)]) for t in big_dev]
+    big_outp = [ctypes.c_void_p(o.data_ptr()) for o in big_out]
+    hg_big = HeadGather(wl.tp, wl.shard, wl.cap, device=dev)
+    big_bytes = 5 * wl.rows * wl.vocab * 2
+
+    if args.pmc_probe:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        fn = call_fn(hg_big, "fused")
+        for _ in range(3):
+            dst.copy_(src)
+        for n in range(6):
+            assert fn(big_ptrs[n % 3], wl.rows, big_outp[n % 3]) == 0
+        torch.cuda.synchronize()
+        log("pmc probe done: 3 x 256 MiB copy, 6 x M=256 fused gather")
+        return 0
+
+    # ---------------- decode: M=1, the timed step --------------------------
+    wd = syn.WORKLOADS["decode"]
+    dec_sets = [syn.shard_set(wd, k) for k in range(wd.pool)]
+    dec_dev = [syn.to_torch_bf16(b, dev) for b in dec_sets]
+    dec_ptrs = [_lib.pointer_array([t[r].data_ptr() for r in range(wd.tp)]) for t in dec_dev]
+    hg = HeadGather(wd.tp, wd.shard, wd.cap, device=dev)
+    n_out = max(args.steps, 1)
+    outs = torch.empty((n_out, wd.rows, wd.vocab), dtype=torch.bfloat16, device=dev)
+    out_ptrs = [ctypes.c_void_p(outs[n].data_ptr()) for n in range(n_out)]
+    fn = call_fn(hg, args.variant)
+
+    log(f"decode warmup {args.warmup}")
+    for n in range(args.warmup):
+        rc = fn(dec_ptrs[n % wd.pool], wd.rows, out_ptrs[n % n_out])
+        if rc:
+            raise _lib.HgError(rc, "warmup")
+    log(f"decode timed {args.steps} gathers ({args.variant})")
+    rcs = 0
+    with Timer(torch, stream) as t_dec:
+        for n in range(args.steps):
+            rcs |= fn(dec_ptrs[n % wd.pool], wd.rows, out_ptrs[n])
+    if rcs:
+        raise _lib.HgError(-abs(rcs), "timed decode loop")
+    us_m1 = t_dec.ms * 1000.0 / args.steps
+
+    # ---------------- M=256 gather: cold (rotating) and back-to-back -------
+    fn_big = call_fn(hg_big, args.variant)
+    for n in range(6):
+        assert fn_big(big_ptrs[n % 3], wl.rows, big_outp[n % 3]) == 0
+    log(f"M=256 timed {args.large_steps} gathers, 3 rotating sets")
+    with Timer(torch, stream) as t_cold:
+        for n in range(args.large_steps):
+            rcs |= fn_big(big_ptrs[n % 3], wl.rows, big_outp[n % 3])
+    with Timer(torch, stream) as t_hot:
+        for n in range(args.large_steps):
+            rcs |= fn_big(big_ptrs[0], wl.rows, big_outp[0])
+    if rcs:
+        raise _lib.HgError(-abs(rcs), "timed M=256 loop")
+    us_cold = t_cold.ms * 1000.0 / args.large_steps
+    us_hot = t_hot.ms * 1000.0 / args.large_steps
+    gbps_cold = big_bytes / (us_cold * 1e-6) / 1e9
+    gbps_hot = big_bytes / (us_hot * 1e-6) / 1e9
+
+    # ---------------- mailbox state after the runs --------------------------
+    armed = torch.full((wd.cap, wd.vocab // 2), -(1 << 31), dtype=torch.int32, device=dev)
+    armed_big = torch.full((wl.cap, wl.vocab // 2), -(1 << 31), dtype=torch.int32, device=dev)
+    for p in (0, 1):
+        if not torch.equal(hg.mailbox(p).view(torch.int32), armed):
+            log("FAIL: decode mailbox not all-sentinel after the run")
+            return 1
+        if not torch.equal(hg_big.mailbox(p).view(torch.int32), armed_big):
+            log("FAIL: M=256 mailbox not all-sentinel after the run")
+            return 1
+    if hg.poll_status() != _lib.HG_OK or hg_big.poll_status() != _lib.HG_OK:
+        log("FAIL: a bounded poll gave up")
+        return 1
+
+    # ---------------- cpu_baseline: the oracle, and the output check --------
+    cpu = None
+    if not args.no_cpu:
+        from oracle import gather as og
+
+        log("cpu baseline: oracle on the decode sets (M=1) and one M=256 set")
+        samples = []
+        want_dec = []
+        t_end = time.perf_counter() + 10.0
+        n = 0
+        while n < 1000 and (n < wd.pool or time.perf_counter() < t_end):
+            t0 = time.perf_counter()
+            r = og.gather_definition(list(dec_sets[n % wd.pool]))
+            samples.append(time.perf_counter() - t0)
+            if n < wd.pool:
+                want_dec.append(r)
+            n += 1
+        t0 = time.perf_counter()
+        want_big = og.gather_definition(list(big_sets[0]))
+        big_cpu_s = time.perf_counter() - t0
+        us_cpu = statistics.median(samples) * 1e6
+        cpu = {"value": round(us_cpu, 2), "unit": "us per gather (M=1)", "cores": 1,
+               "kind": "oracle",
+               "sample": f"oracle.gather.gather_definition (numpy, single thread) on the decode "
+                         f"input sets: median of {len(samples)} calls; plus one M=256 call",
+               "m256_gbps_algorithmic": round(big_bytes / big_cpu_s / 1e9, 3),
+               "os_cpu_count": os.cpu_count(),
+               "affinity": len(os.sched_getaffinity(0)),
+               "torch_threads": torch.get_num_threads()}
+        # the GPU outputs of the timed loop (call n used set n % pool) against the oracle
+        got = outs[: wd.pool].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        for k in range(min(wd.pool, args.steps)):
+            if not np.array_equal(got[k], want_dec[k]):
+                log(f"FAIL: decode output of call {k} differs from the oracle")
+                return 1
+        if not np.array_equal(syn.from_torch_bf16(big_out[0]), want_big):
+            log("FAIL: M=256 output differs from the oracle")
+            return 1
+
+    # ---------------- counters (only if taken on this kernel source) --------
+    traffic = None
+    if os.path.exists(COUNTERS):
+        with open(COUNTERS) as f:
+            c = json.load(f)
+        if c.get("kernel_source_sha256_16") == kernel_source_hash() and c.get("variant") == args.variant:
+            traffic = c.get("traffic_bytes_per_launch")
+
+    dec_bytes = 5 * wd.rows * wd.vocab * 2
+    line = {
+        "metric": METRIC,
+        "value": round(us_m1, 3),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_dec.ms / args.steps, 6),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": "decode gather: TP=8 virtual ranks, V=163840 (shard 20480 BF16), "
+                               "M=1, cap=8, back-to-back calls on one stream, inputs resident",
+                   "variant": args.variant, "tp": wd.tp, "vocab": wd.vocab, "rows": wd.rows,
+                   "cap": wd.cap},
+        "large_m": {"workload": "gather TP=8, V=163840, M=256, cap=256, 3 rotating buffer sets",
+                    "us_per_gather_cold": round(us_cold, 3),
+                    "gbps_algorithmic_cold": round(gbps_cold, 1),
+                    "us_per_gather_back_to_back": round(us_hot, 3),
+                    "gbps_algorithmic_back_to_back": round(gbps_hot, 1),
+                    "algorithmic_bytes_per_gather": big_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(gbps_cold, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(gbps_cold / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "k_fused (M=256 gather, cold)" if args.variant == "fused"
+                               else "k_push + k_collect (M=256 gather, cold)"},
+        "roofline_m1": {"bound": "latency", "achieved": round(dec_bytes / (us_m1 * 1e-6) / 1e9, 1),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(dec_bytes / (us_m1 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "cpu_baseline": cpu,
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,196 @@
+/*
+ * hg.h -- one-shot Lamport-mailbox gather of vocab-parallel lm_head logits,
+ * for AMD MI355X (gfx950). C ABI of libhg.so.
+ *
+ * The operation (vLLM API documentation page
+ * "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.logits_gather",
+ * module description and HeadGather class description):
+ *
+ *   Each of TP ranks holds a [M, S] BF16 shard of the vocab-parallel lm_head
+ *   logits (S = shard = V / TP). A gather call produces the [M, V] BF16 logits
+ *   with rank r at columns r * S -- the layout of NCCL's all-gather -- through
+ *   a mailbox of 2 parities x cap rows x V BF16 that is armed with a sentinel.
+ *   A word is two adjacent BF16 elements (2k, 2k+1) of a row, read as a
+ *   little-endian 32-bit value. The sentinel word is the pair (+0, -0),
+ *   0x80000000; a shard word equal to it is written into the mailbox as
+ *   (+0, +0), 0x00000000, every other byte moves unchanged. The consumer polls
+ *   each mailbox word until it is not the sentinel, copies the row to the
+ *   output and re-arms the mailbox. The parity alternates per served call.
+ *
+ * Here the TP ranks are virtual: every shard and the mailbox sit in the HBM of
+ * the one device that was current at hg_create, and one kernel does the push,
+ * poll, copy and re-arm for all of them.
+ *
+ * Conventions for every entry point:
+ *  - Return value: HG_OK (0) on success; HG_EDECLINE (1) when the call is not
+ *    served -- nothing was enqueued, no state changed, and the caller takes
+ *    the stock path (hg_stock_gather, or its own all-gather); a negative
+ *    HG_E* code on error (no state changed unless stated).
+ *  - `stream` is a hipStream_t passed as void* (NULL: the null stream). Device
+ *    work is enqueued on it and the call returns without waiting, unless
+ *    stated otherwise.
+ *  - Every device pointer must be 16-byte aligned and belong to the context's
+ *    device, which must be the current device at the call (else HG_EINVAL).
+ *  - Ownership: the context owns its mailbox and a 256-byte status block;
+ *    the caller owns every shard, output and weight buffer.
+ *  - Ordering: all calls on one context are issued from one host thread at a
+ *    time, on one stream, in call order. Two uses of one parity are then
+ *    separated by a use of the other, and a push into a parity starts only
+ *    after the previous kernel on it finished re-arming (API page, HeadGather
+ *    class description). This is documented, not enforced: calls on different
+ *    streams can race.
+ */
+#ifndef HG_H
+#define HG_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Largest number of (virtual) ranks a context accepts. */
+#define HG_MAX_TP 64
+
+/* Status codes. */
+#define HG_OK 0
+#define HG_EDECLINE 1  /* not served: take the stock path; nothing enqueued     */
+#define HG_EINVAL (-1) /* bad argument (sizes, null or misaligned pointer, ...) */
+#define HG_ENOMEM (-2) /* device allocation failed                             */
+#define HG_EHIP (-3)   /* a HIP runtime call failed (see hg_last_error_detail)  */
+#define HG_ETIMEOUT (-4) /* a bounded poll gave up (reported by hg_poll_status)  */
+#define HG_ESTATE (-5) /* split-variant call out of order                       */
+
+typedef struct hg_ctx hg_ctx;
+
+/*
+ * Create a gather context for `tp` virtual ranks of `shard` BF16 columns each
+ * and up to `cap` rows per call (API page, HeadGather.__init__ source: the
+ * mailbox is allocated with 2 x cap x (shard/2 * tp) 32-bit words and armed;
+ * the device is synchronised before returning; the parity starts at 0).
+ *
+ * Refused with HG_EINVAL: out == NULL; tp < 2 or tp > HG_MAX_TP (a TP of 1 is
+ * declined by install_logits_gather); shard < 8 or shard % 8 != 0 (the
+ * _install_gather source refuses other shard widths); cap < 1; a mailbox of
+ * 2^31 or more 16-byte vectors per parity. HG_ENOMEM / HG_EHIP on device
+ * failures. On success *out holds the context; on failure *out is NULL.
+ * Served row counts are 1..cap.
+ */
+int hg_create(int tp, int shard, int cap, hg_ctx **out);
+
+/* Free the mailbox and the context. NULL-safe. Synchronises the device first
+ * so no enqueued kernel still uses the mailbox. */
+int hg_destroy(hg_ctx *h);
+
+/* Re-arm both parities to all-sentinel, reset the parity to 0 and drop any
+ * pending split push (stream-ordered on `stream`). Recovery after an error. */
+int hg_arm(hg_ctx *h, void *stream);
+
+/*
+ * The gather, fused in one kernel launch (API page, HeadGather.__call__
+ * source and module description).
+ *
+ * shards: host array of tp device pointers; shards[r] is rank r's [m][shard]
+ *         BF16 block, row-major, contiguous (row stride = shard elements).
+ * m:      rows to gather this call.
+ * out:    device [m][tp*shard] BF16, row-major; receives rank r's row i at
+ *         columns r*shard .. r*shard+shard-1 of row i, every sentinel word
+ *         rewritten to zero. Must not overlap the shards or the mailbox.
+ *
+ * HG_EDECLINE (stock path, parity unchanged) when m == 0, m > cap, or the
+ * stream is capturing a graph (host-side parity cannot alternate under
+ * replay). HG_EINVAL for m < 0, NULL / misaligned / overlapping pointers.
+ * HG_ESTATE if a split push is pending. On HG_OK the parity flips.
+ */
+int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, void *stream);
+
+/*
+ * Split variant, first half: push the shards into the current parity's rows
+ * 0..m-1 (sentinel words rewritten) and leave the call pending. Same
+ * arguments, declines and errors as hg_gather; HG_ESTATE if a push is already
+ * pending. The parity does not change.
+ */
+int hg_push(hg_ctx *h, const void *const *shards, int m, void *stream);
+
+/*
+ * Split variant, partial push: only the ranks whose bit is set in `ranks`
+ * (bit r = rank r) push their fragments; shards[r] is read only for those.
+ * Each rank of a real TP group pushes its own fragment on its own schedule;
+ * this entry point lets virtual ranks do the same. Pushes of disjoint rank
+ * sets with the same m accumulate into one pending call. HG_ESTATE if a rank
+ * already pushed into the pending call or m differs from it; HG_EINVAL if
+ * `ranks` is empty or names a rank >= tp. A collect issued while some rank
+ * has not pushed polls words that never arrive: its bounded poll gives up
+ * (see hg_set_poll_limit / hg_poll_status).
+ */
+int hg_push_ranks(hg_ctx *h, const void *const *shards, int m, unsigned long long ranks,
+                  void *stream);
+
+/*
+ * Split variant, second half: poll rows 0..m-1 of the pending parity until no
+ * word is the sentinel, copy them to `out` ([m][tp*shard] BF16) and re-arm
+ * them; then flip the parity. HG_ESTATE unless a push of the same m is
+ * pending (from any set of ranks); HG_EDECLINE (nothing changes) if the
+ * stream is capturing.
+ */
+int hg_collect(hg_ctx *h, int m, void *out, void *stream);
+
+/*
+ * The stock gather's single-device share (API page, module description: the
+ * all-gather into [TP, M, V/TP] followed by a copy to [M, V]): rank-order
+ * concatenation into out[m][tp*shard], every byte unchanged (no sentinel
+ * rewrite). Needs no context; tp in [1, HG_MAX_TP], shard % 8 == 0, m >= 0.
+ */
+int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *out, void *stream);
+
+/* The parity the next served call will use (0 or 1), or HG_EINVAL. */
+int hg_parity(const hg_ctx *h);
+
+/* Read-only view of one parity of the mailbox, for inspection by tests:
+ * *dev = device address of [cap][tp*shard] BF16, *bytes = its size. */
+int hg_mailbox(const hg_ctx *h, int parity, const void **dev, size_t *bytes);
+
+/* Enqueue a copy of one parity of the mailbox ([cap][tp*shard] BF16) into the
+ * caller's device buffer `dst` (same size, must not overlap the mailbox). */
+int hg_copy_mailbox(const hg_ctx *h, int parity, void *dst, void *stream);
+
+/*
+ * Bound every poll: a lane that re-reads a sentinel word more than `spins`
+ * times gives up, counts a timeout in the context's status block and
+ * continues (its output then holds sentinel words). 0 restores the default
+ * (2^24 re-reads). Takes effect for calls enqueued afterwards.
+ */
+int hg_set_poll_limit(hg_ctx *h, unsigned long long spins);
+
+/* Wait for `stream`, then report and clear the poll-timeout count:
+ * HG_OK if no poll gave up since the last check, HG_ETIMEOUT otherwise.
+ * HG_EINVAL if the stream is capturing. */
+int hg_poll_status(hg_ctx *h, void *stream);
+
+/* Launch-shape knobs (for sweeps). Values are validated; 0 selects the
+ * built-in choice where noted. */
+#define HG_TUNE_FUSED_BLOCK 1 /* threads per workgroup: 64, 128, 256, 512, 1024          */
+#define HG_TUNE_FUSED_VPT 2   /* 16-byte vectors per lane per chunk: 0 (auto), 1, 2, 4, 8 */
+#define HG_TUNE_FUSED_GRID 3  /* workgroup cap: 0 (co-resident limit) or >= 1            */
+#define HG_TUNE_SPLIT_BLOCK 4 /* as HG_TUNE_FUSED_BLOCK, for push / collect / stock      */
+#define HG_TUNE_SPLIT_VPT 5   /* as HG_TUNE_FUSED_VPT, for push / collect / stock        */
+#define HG_TUNE_POLL_SKEW 6   /* fused: workgroup b polls what b-skew pushed; >= 1       */
+#define HG_TUNE_PUSH_MODE 7   /* 0: agent-coherent stores; 1: plain stores + release fence */
+int hg_set_tuning(hg_ctx *h, int knob, int value);
+int hg_get_tuning(const hg_ctx *h, int knob, int *value);
+
+/* Workgroups the fused kernel may keep resident at once on the context's
+ * device with the current block size (the grid cap), or a negative code. */
+int hg_fused_grid_limit(const hg_ctx *h);
+
+/* Static description of a status code. */
+const char *hg_strerror(int code);
+
+/* The last HIP error seen by this thread inside the library ("" if none). */
+const char *hg_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HG_H */

@@ -36,7 +36,11 @@ Readings taken where the pages leave a step open (also listed in the design doc):
   ``shard % 8``; a zero shard is refused here as well).
 * Split variant: ``push`` fills the current parity and leaves it pending;
   ``collect`` of the same row count completes the call and flips the parity.
-  Any other order is a state error.
+  Any other order is a state error. Ranks may push separately
+  (``push_ranks``), as each rank of a real TP group pushes its own fragment;
+  a collect while some rank has not pushed is a poll that never completes: a
+  bounded poll gives up (``ETIMEOUT``), its output keeps the sentinel words it
+  read, and the rows are re-armed and the parity flipped as for any call.
 """
 
 from __future__ import annotations
@@ -48,7 +52,7 @@ import numpy as np
 SENT_WORD = 0x80000000
 
 #: Status values of the protocol simulator, mirroring the C boundary.
-OK, DECLINE, EINVAL, ESTATE = 0, 1, -1, -5
+OK, DECLINE, EINVAL, ETIMEOUT, ESTATE = 0, 1, -1, -4, -5
 
 
 # ---------------------------------------------------------------------------
@@ -158,6 +162,7 @@ class MailboxSim:
         self.box = np.empty((2, cap, self.words_per_row), dtype=np.uint32)
         self.parity = 0
         self.pending: tuple[int, int] | None = None  # (m, parity) of a split push
+        self.pushed: set[int] = set()                # ranks that pushed into it
         self.arm()
 
     # -- state ------------------------------------------------------------
@@ -166,6 +171,7 @@ class MailboxSim:
         self.box[...] = np.uint32(SENT_WORD)
         self.parity = 0
         self.pending = None
+        self.pushed = set()
 
     def served(self, m: int, capturing: bool = False) -> bool:
         """Eligibility of a call (``HeadGather.__call__`` source): the row count
@@ -174,17 +180,17 @@ class MailboxSim:
         return 1 <= m <= self.cap and not capturing
 
     # -- the four steps ----------------------------------------------------
-    def _push(self, p: int, shards, m: int) -> None:
+    def _push(self, p: int, shards, m: int, ranks=None) -> None:
         half = self.shard // 2
-        for r in range(self.tp):
+        for r in (range(self.tp) if ranks is None else sorted(ranks)):
             rows = np.asarray(shards[r], dtype=np.uint16)
             if rows.shape != (m, self.shard):
                 raise ValueError(f"rank {r} shard has shape {rows.shape}, expected {(m, self.shard)}")
             self.box[p, :m, r * half:(r + 1) * half] = rewrite_sentinel(pack_words(rows))
 
-    def _poll(self, p: int, m: int) -> np.ndarray:
+    def _poll(self, p: int, m: int, bounded: bool = False) -> np.ndarray:
         rows = self.box[p, :m, :].copy()
-        if np.any(rows == np.uint32(SENT_WORD)):
+        if not bounded and np.any(rows == np.uint32(SENT_WORD)):
             raise AssertionError("a polled word is still the sentinel after the push")
         return rows
 
@@ -213,29 +219,43 @@ class MailboxSim:
         return OK, unpack_words(words)
 
     def push(self, shards, capturing: bool = False) -> int:
-        """Split variant, first half: the push into the current parity."""
-        m = int(np.asarray(shards[0]).shape[0])
-        if self.pending is not None:
+        """Split variant, first half: every rank pushes into the current parity."""
+        return self.push_ranks(shards, range(self.tp), capturing)
+
+    def push_ranks(self, shards, ranks, capturing: bool = False) -> int:
+        """Split variant: the listed ranks push their fragments into the
+        current parity (``shards[r]`` is read only for those ranks). Pushes of
+        disjoint rank sets with the same row count accumulate into one pending
+        call; a rank pushing twice, or another row count, is a state error."""
+        ranks = set(int(r) for r in ranks)
+        m = int(np.asarray(shards[min(ranks)]).shape[0]) if ranks else 0
+        if not ranks or any(r < 0 or r >= self.tp for r in ranks):
+            return EINVAL
+        if self.pending is not None and (self.pending[0] != m or ranks & self.pushed):
             return ESTATE
         if not self.served(m, capturing):
             return DECLINE
-        self._push(self.parity, shards, m)
-        self.pending = (m, self.parity)
+        p = self.parity if self.pending is None else self.pending[1]
+        self._push(p, shards, m, ranks)
+        self.pending = (m, p)
+        self.pushed |= ranks
         return OK
 
     def collect(self, m: int, capturing: bool = False):
         """Split variant, second half: poll, copy, re-arm, flip the parity.
-        Returns ``(status, out)``."""
+        Returns ``(status, out)``; ``ETIMEOUT`` when some rank never pushed."""
         if capturing:
             return DECLINE, None
         if self.pending is None or self.pending[0] != m:
             return ESTATE, None
         _, p = self.pending
-        words = self._poll(p, m)
+        complete = len(self.pushed) == self.tp
+        words = self._poll(p, m, bounded=not complete)
         self._rearm(p, m)
         self.pending = None
+        self.pushed = set()
         self.parity ^= 1
-        return OK, unpack_words(words)
+        return (OK if complete else ETIMEOUT), unpack_words(words)
 
     def mailbox_bf16(self, parity: int) -> np.ndarray:
         """Mailbox of one parity as ``[cap, V]`` BF16 patterns."""

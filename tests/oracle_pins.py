@@ -231,6 +231,44 @@ def check_protocol(g) -> None:
         assert sim.parity == 0 and sim.pending is None and np.all(sim.box == sent)
 
 
+def check_partial_push(g) -> None:
+    """Ranks pushing separately: disjoint rank sets accumulate into one call;
+    a collect with a rank missing gives up (ETIMEOUT) with that rank's columns
+    still the sentinel, and re-arms and flips like any call."""
+    rng = np.random.default_rng(15)
+    sent = torch_sentinel()
+    for tp, s, cap, m in [(2, 8, 1, 1), (4, 16, 3, 2), (8, 24, 2, 2), (3, 8, 4, 4)]:
+        sim = g.MailboxSim(tp, s, cap)
+        shards = rand_bits(rng, (tp, m, s))
+        force_pairs(shards, rng, min(4, tp * m * s // 2))
+        want = g.gather_definition(list(shards))
+        # all ranks, in a shuffled order of disjoint groups
+        order = rng.permutation(tp)
+        groups = np.array_split(order, min(3, tp))
+        for grp in groups:
+            assert sim.push_ranks(list(shards), [int(r) for r in grp]) == g.OK
+        assert sim.push_ranks(list(shards), [int(order[0])]) == g.ESTATE  # rank pushes twice
+        status, out = sim.collect(m)
+        assert status == g.OK and np.array_equal(out, want) and sim.parity == 1
+        assert np.all(sim.box == sent)
+        # one rank missing: the poll gives up
+        missing = int(rng.integers(0, tp))
+        assert sim.push_ranks(list(shards), [r for r in range(tp) if r != missing]) == g.OK
+        status, out = sim.collect(m)
+        assert status == g.ETIMEOUT and sim.parity == 0
+        cols = slice(missing * s, (missing + 1) * s)
+        assert np.all(torch_words(np.ascontiguousarray(out[:, cols])) == sent)
+        keep = np.ones(tp * s, bool)
+        keep[cols] = False
+        assert np.array_equal(out[:, keep], want[:, keep])
+        assert np.all(sim.box == sent)
+        # a second push with another row count joins no pending call
+        if cap >= 2:
+            assert sim.push_ranks(list(shards[:, :1]), [0]) == g.OK
+            assert sim.push_ranks(list(shards[:, :2]), [1]) == g.ESTATE
+            sim.arm()
+
+
 def check_create_rules(g) -> None:
     for shard in range(0, 65):
         assert g.create_ok(2, shard, 1) == (shard >= 8 and shard % 8 == 0), shard
@@ -242,7 +280,7 @@ def check_create_rules(g) -> None:
 
 GATHER_CHECKS = [check_sentinel_constant, check_packing, check_golden_gather, check_layout_nccl,
                  check_value_equivalence_and_xor, check_exhaustive_tiny, check_protocol,
-                 check_create_rules]
+                 check_partial_push, check_create_rules]
 
 
 # ---------------------------------------------------------------------------

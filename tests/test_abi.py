@@ -1,0 +1,99 @@
+"""The C ABI without a GPU: libhg.so loads, exports every function that
+include/hg.h declares, and its host-side argument checks return the documented
+codes before touching a device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from tp_vocab_logits_amd import _lib
+from oracle import gather as oracle_gather
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"#[^\n]*", " ", text)
+    return sorted(set(re.findall(r"\b(hg_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = declared_functions()
+    for required in ["hg_create", "hg_arm", "hg_gather", "hg_destroy", "hg_push", "hg_collect",
+                     "hg_parity", "hg_mailbox", "hg_strerror"]:
+        assert required in names
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with hg.h"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_create_validation_matches_the_oracle_rules():
+    lib = _lib.lib()
+    h = ctypes.c_void_p(1)
+    for tp in range(0, 5):
+        for shard in range(0, 41):
+            for cap in (0, 1, 3):
+                if oracle_gather.create_ok(tp, shard, cap):
+                    continue  # a valid create needs a device; not run here
+                rc = lib.hg_create(tp, shard, cap, ctypes.byref(h))
+                assert rc == _lib.HG_EINVAL, (tp, shard, cap)
+                assert not h.value
+    assert lib.hg_create(65, 8, 1, ctypes.byref(h)) == _lib.HG_EINVAL  # above HG_MAX_TP
+    assert lib.hg_create(2, 8, 1, None) == _lib.HG_EINVAL
+    # a mailbox of 2^31 vectors per parity or more is refused
+    assert lib.hg_create(8, 8 * 2 ** 20, 2 ** 8, ctypes.byref(h)) == _lib.HG_EINVAL
+
+
+def test_null_context_paths():
+    lib = _lib.lib()
+    null = ctypes.c_void_p()
+    ptrs = _lib.pointer_array([16, 32])
+    assert lib.hg_destroy(null) == _lib.HG_OK
+    assert lib.hg_arm(null, None) == _lib.HG_EINVAL
+    assert lib.hg_gather(null, ptrs, 1, ctypes.c_void_p(64), None) == _lib.HG_EINVAL
+    assert lib.hg_push(null, ptrs, 1, None) == _lib.HG_EINVAL
+    assert lib.hg_push_ranks(null, ptrs, 1, 1, None) == _lib.HG_EINVAL
+    assert lib.hg_collect(null, 1, ctypes.c_void_p(64), None) == _lib.HG_EINVAL
+    assert lib.hg_parity(null) == _lib.HG_EINVAL
+    dev, nbytes = ctypes.c_void_p(), ctypes.c_size_t()
+    assert lib.hg_mailbox(null, 0, ctypes.byref(dev), ctypes.byref(nbytes)) == _lib.HG_EINVAL
+    assert lib.hg_copy_mailbox(null, 0, ctypes.c_void_p(64), None) == _lib.HG_EINVAL
+    assert lib.hg_set_poll_limit(null, 5) == _lib.HG_EINVAL
+    assert lib.hg_poll_status(null, None) == _lib.HG_EINVAL
+    assert lib.hg_set_tuning(null, _lib.TUNE_FUSED_BLOCK, 256) == _lib.HG_EINVAL
+    v = ctypes.c_int()
+    assert lib.hg_get_tuning(null, _lib.TUNE_FUSED_BLOCK, ctypes.byref(v)) == _lib.HG_EINVAL
+    assert lib.hg_fused_grid_limit(null) == _lib.HG_EINVAL
+
+
+def test_stock_gather_argument_checks():
+    lib = _lib.lib()
+    ptrs = _lib.pointer_array([16, 32])
+    out = ctypes.c_void_p(4096)
+    assert lib.hg_stock_gather(0, 8, ptrs, 1, out, None) == _lib.HG_EINVAL
+    assert lib.hg_stock_gather(2, 12, ptrs, 1, out, None) == _lib.HG_EINVAL
+    assert lib.hg_stock_gather(2, 8, ptrs, -1, out, None) == _lib.HG_EINVAL
+    assert lib.hg_stock_gather(2, 8, ptrs, 0, out, None) == _lib.HG_OK  # nothing to do
+    assert lib.hg_stock_gather(2, 8, ptrs, 1, ctypes.c_void_p(4100), None) == _lib.HG_EINVAL
+    bad = _lib.pointer_array([16, 40])  # misaligned rank-1 pointer
+    assert lib.hg_stock_gather(2, 8, bad, 1, out, None) == _lib.HG_EINVAL
+    overlap = _lib.pointer_array([16, 4096])  # rank 1 overlaps the output
+    assert lib.hg_stock_gather(2, 8, overlap, 1, out, None) == _lib.HG_EINVAL
+
+
+def test_status_strings():
+    lib = _lib.lib()
+    for code in (_lib.HG_OK, _lib.HG_EDECLINE, _lib.HG_EINVAL, _lib.HG_ENOMEM, _lib.HG_EHIP,
+                 _lib.HG_ETIMEOUT, _lib.HG_ESTATE, 1234):
+        assert lib.hg_strerror(code)
+    assert lib.hg_last_error_detail() is not None

@@ -116,6 +116,22 @@ class _SimArmKeepsParity(gather.MailboxSim):
         self.parity = p
 
 
+class _SimCollectIgnoresMissing(gather.MailboxSim):
+    def collect(self, m, capturing=False):
+        self.pushed = set(range(self.tp)) if self.pending is not None else self.pushed
+        return super().collect(m, capturing)
+
+
+class _SimPartialPushAll(gather.MailboxSim):
+    def push_ranks(self, shards, ranks, capturing=False):
+        ranks = set(int(r) for r in ranks)
+        status = super().push_ranks(shards, ranks, capturing)
+        if status == gather.OK:
+            m, p = self.pending
+            self._push(p, shards, m)
+        return status
+
+
 def _lm_head_untransposed(x_bits, w_bits):
     x, w = gemm.bf16_to_f64(x_bits), gemm.bf16_to_f64(w_bits)
     return x @ w.reshape(w.shape[1], w.shape[0])
@@ -170,6 +186,8 @@ MUTANTS = [
     ("serves cap + 1 rows", gather, {"MailboxSim": _SimServesCapAndOne}),
     ("serves under graph capture", gather, {"MailboxSim": _SimIgnoresCapture}),
     ("arm keeps the parity", gather, {"MailboxSim": _SimArmKeepsParity}),
+    ("collect ignores a missing rank", gather, {"MailboxSim": _SimCollectIgnoresMissing}),
+    ("partial push writes every rank", gather, {"MailboxSim": _SimPartialPushAll}),
     ("lm_head weight not transposed", gemm, {"lm_head_shard": _lm_head_untransposed}),
     ("lm_head drops a term", gemm, {"lm_head_shard": _lm_head_dropped_term}),
     ("lm_head loses a sign", gemm, {"lm_head_shard": _lm_head_wrong_sign}),

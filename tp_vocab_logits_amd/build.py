@@ -1,0 +1,68 @@
+"""Build libhg.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+Usage: ``python -m tp_vocab_logits_amd.build`` (or ``__graft_entry__.build()``).
+Always recompiles; the result replaces ``tp_vocab_logits_amd/libhg.so``
+atomically.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libhg.so")
+SOURCES = ["hg_api.cpp", "hg_kernels.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found: cannot build libhg.so")
+
+
+def compile_command(output: str) -> list[str]:
+    return [
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
+        # keep the compiler from forming packed-FP32 instructions
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-I", INCLUDE, "-I", CSRC, "-x", "hip",
+        *[os.path.join(CSRC, s) for s in SOURCES],
+        "-o", output,
+    ]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libhg.so and return its path. Raises on a compiler error."""
+    fd, tmp = tempfile.mkstemp(prefix="libhg.", suffix=".so.tmp", dir=PKG)
+    os.close(fd)
+    try:
+        cmd = compile_command(tmp)
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        # hipcc's host pass does not know the packed-fp32 feature and says so
+        noise = [ln for ln in (res.stderr or "").splitlines()
+                 if ln.strip() and "packed-fp32-ops" not in ln and "not a recognized feature" not in ln]
+        if res.returncode != 0:
+            raise RuntimeError("libhg.so build failed:\n" + (res.stderr or res.stdout))
+        if verbose and noise:
+            print("\n".join(noise), file=sys.stderr)
+        os.replace(tmp, LIB)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

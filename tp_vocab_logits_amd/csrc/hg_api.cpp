@@ -1,0 +1,473 @@
+// Host side of libhg.so: the context, argument checks, parity state and
+// launch shapes of the one-shot Lamport-mailbox logits gather. The C ABI is
+// declared (and documented) in include/hg.h.
+//
+// Behaviour follows the vLLM API documentation page
+// "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.logits_gather":
+//  - construction allocates the two-parity mailbox, arms it and synchronises
+//    the device; the parity starts at 0 (HeadGather.__init__ source);
+//  - a call is served only for a served row count and outside graph capture,
+//    otherwise the caller takes the stock path and nothing changes; a served
+//    call takes the current parity and flips it (HeadGather.__call__ source);
+//  - shard widths that are not a multiple of 8 are refused (_install_gather
+//    source) and so is a TP of 1 (install_logits_gather source).
+
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+
+#include "hg_internal.h"
+
+#define HG_API extern "C" __attribute__((visibility("default")))
+
+using hg::Geometry;
+using hg::ShardTable;
+using hg::u32x4;
+
+namespace {
+
+constexpr unsigned long long kDefaultPollLimit = 1ull << 24;
+constexpr int kStatusBytes = 256;
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e, const char *where) {
+  snprintf(g_last_error, sizeof g_last_error, "%s: %s (%d)", where, hipGetErrorString(e),
+           static_cast<int>(e));
+  return HG_EHIP;
+}
+
+#define HIP_TRY(expr)                                 \
+  do {                                                \
+    hipError_t e_ = (expr);                           \
+    if (e_ != hipSuccess) return hip_fail(e_, #expr); \
+  } while (0)
+
+struct Tuning {
+  int fused_block = 256;
+  int fused_vpt = 0;  // 0: by row count
+  int fused_grid = 0;  // 0: co-resident limit
+  int split_block = 256;
+  int split_vpt = 0;
+  int poll_skew = 1;
+  int push_mode = hg::kPushAgentStores;
+};
+
+bool valid_block(int b) { return b == 64 || b == 128 || b == 256 || b == 512 || b == 1024; }
+bool valid_vpt(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8; }
+
+// Vectors per lane for a launch moving `vectors` 16-byte vectors per phase:
+// few vectors per lane when the call is small (latency: spread it over many
+// waves), more when it is large (bandwidth: more bytes in flight per lane).
+int auto_vpt(long long vectors, int cus) {
+  const long long lanes = static_cast<long long>(cus) * 256;
+  if (vectors <= lanes) return 1;
+  if (vectors <= 4 * lanes) return 2;
+  return 4;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na && nb && x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+struct hg_ctx {
+  int tp = 0, shard = 0, cap = 0;
+  int device = -1;
+  int cus = 0;
+  long long vv = 0;             // 16-byte vectors per mailbox / output row
+  u32x4 *box = nullptr;         // [2][cap][vv]
+  unsigned *status = nullptr;   // poll-timeout counter (first word)
+  int parity = 0;
+  int pending_m = -1;           // split push awaiting its collect
+  int pending_parity = 0;
+  unsigned long long pending_ranks = 0;  // ranks that pushed into it
+  unsigned long long poll_limit = kDefaultPollLimit;
+  Tuning tune;
+  int fused_per_cu[4][2] = {};  // [log2 vpt][mode] resident blocks per CU at tune.fused_block
+
+  u32x4 *parity_box(int p) const { return box + static_cast<long long>(p) * cap * vv; }
+  size_t row_bytes() const { return static_cast<size_t>(vv) * 16; }
+};
+
+namespace {
+
+int vpt_index(int vpt) { return vpt == 1 ? 0 : vpt == 2 ? 1 : vpt == 4 ? 2 : 3; }
+
+int refresh_occupancy(hg_ctx *h) {
+  for (int i = 0; i < 4; ++i)
+    for (int mode = 0; mode < 2; ++mode) {
+      int n = 0;
+      HIP_TRY(hg::fused_blocks_per_cu(1 << i, mode, h->tune.fused_block, &n));
+      h->fused_per_cu[i][mode] = n;
+    }
+  return HG_OK;
+}
+
+int check_device(const hg_ctx *h) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev));
+  if (dev != h->device) return HG_EINVAL;
+  return HG_OK;
+}
+
+// HG_OK if not capturing, HG_EDECLINE if capturing, HG_EHIP on failure.
+int capture_state(hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  const hipError_t e = hipStreamIsCapturing(s, &st);
+  if (e == hipErrorStreamCaptureImplicit || e == hipErrorStreamCaptureUnsupported) {
+    (void)hipGetLastError();
+    return HG_EDECLINE;
+  }
+  if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+  return st == hipStreamCaptureStatusNone ? HG_OK : HG_EDECLINE;
+}
+
+unsigned long long all_ranks(int tp) { return tp >= 64 ? ~0ull : (1ull << tp) - 1; }
+
+// Checks the shard pointers of an m-row call for the ranks in `ranks` and
+// fills the kernel table (other entries stay null and are never read).
+int load_shards(int tp, int shard, const void *const *shards, int m, unsigned long long ranks,
+                ShardTable *t, const void *out, size_t out_bytes, const void *box,
+                size_t box_bytes) {
+  if (!shards) return HG_EINVAL;
+  memset(t, 0, sizeof *t);
+  const size_t shard_bytes = static_cast<size_t>(m) * shard * 2;
+  for (int r = 0; r < tp; ++r) {
+    if (!((ranks >> r) & 1ull)) continue;
+    const void *p = shards[r];
+    if (!p || !aligned16(p)) return HG_EINVAL;
+    if (overlaps(p, shard_bytes, out, out_bytes)) return HG_EINVAL;
+    if (box && overlaps(p, shard_bytes, box, box_bytes)) return HG_EINVAL;
+    t->p[r] = static_cast<const u32x4 *>(p);
+  }
+  return HG_OK;
+}
+
+int split_grid(const hg_ctx *h, const Geometry &g, int block) {
+  const int waves = block / 64;
+  const long long tiles = (static_cast<long long>(g.chunks) + waves - 1) / waves;
+  const long long cap = static_cast<long long>(h->cus) * 16;
+  return static_cast<int>(tiles < cap ? tiles : cap);
+}
+
+int fused_limit(const hg_ctx *h, int vpt) {
+  const int per_cu = h->fused_per_cu[vpt_index(vpt)][h->tune.push_mode];
+  long long lim = static_cast<long long>(per_cu) * h->cus;
+  if (h->tune.fused_grid > 0 && h->tune.fused_grid < lim) lim = h->tune.fused_grid;
+  return static_cast<int>(lim);
+}
+
+int pick_vpt(const hg_ctx *h, int knob, int m) {
+  return knob ? knob : auto_vpt(static_cast<long long>(m) * h->vv, h->cus);
+}
+
+// Common checks of hg_gather / hg_push_ranks. Returns HG_OK when the call is
+// served. `joining`: a push that may join a pending call of the same m.
+int check_call(hg_ctx *h, const void *const *shards, int m, unsigned long long ranks,
+               bool joining, const void *out, void *stream, ShardTable *table) {
+  if (!h || m < 0) return HG_EINVAL;
+  if (ranks == 0 || (ranks & ~all_ranks(h->tp))) return HG_EINVAL;
+  if (h->pending_m >= 0) {
+    if (!joining || m != h->pending_m || (ranks & h->pending_ranks)) return HG_ESTATE;
+  }
+  if (m == 0 || m > h->cap) return HG_EDECLINE;
+  const int cs = capture_state(static_cast<hipStream_t>(stream));
+  if (cs != HG_OK) return cs;
+  int rc = check_device(h);
+  if (rc != HG_OK) return rc;
+  const size_t out_bytes = static_cast<size_t>(m) * h->row_bytes();
+  const size_t box_bytes = static_cast<size_t>(2) * h->cap * h->row_bytes();
+  if (out) {
+    if (!aligned16(out) || overlaps(out, out_bytes, h->box, box_bytes)) return HG_EINVAL;
+  }
+  return load_shards(h->tp, h->shard, shards, m, ranks, table, out, out ? out_bytes : 0, h->box,
+                     box_bytes);
+}
+
+}  // namespace
+
+HG_API int hg_create(int tp, int shard, int cap, hg_ctx **out) {
+  if (!out) return HG_EINVAL;
+  *out = nullptr;
+  if (tp < 2 || tp > HG_MAX_TP || shard < 8 || shard % 8 != 0 || cap < 1) return HG_EINVAL;
+  const long long vv = static_cast<long long>(tp) * (shard / 8);
+  if (vv * cap >= (1ll << 31)) return HG_EINVAL;
+
+  hg_ctx *h = new (std::nothrow) hg_ctx;
+  if (!h) return HG_ENOMEM;
+  h->tp = tp;
+  h->shard = shard;
+  h->cap = cap;
+  h->vv = vv;
+  auto fail = [&](int rc) {
+    if (h->box) (void)hipFree(h->box);
+    if (h->status) (void)hipFree(h->status);
+    delete h;
+    return rc;
+  };
+  hipError_t e = hipGetDevice(&h->device);
+  if (e != hipSuccess) return fail(hip_fail(e, "hipGetDevice"));
+  e = hipDeviceGetAttribute(&h->cus, hipDeviceAttributeMultiprocessorCount, h->device);
+  if (e != hipSuccess) return fail(hip_fail(e, "hipDeviceGetAttribute"));
+  const size_t box_bytes = static_cast<size_t>(2) * cap * vv * 16;
+  e = hipMalloc(reinterpret_cast<void **>(&h->box), box_bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(e == hipErrorOutOfMemory ? HG_ENOMEM : hip_fail(e, "hipMalloc(mailbox)"));
+  }
+  e = hipMalloc(reinterpret_cast<void **>(&h->status), kStatusBytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(e == hipErrorOutOfMemory ? HG_ENOMEM : hip_fail(e, "hipMalloc(status)"));
+  }
+  e = hipMemset(h->status, 0, kStatusBytes);
+  if (e != hipSuccess) return fail(hip_fail(e, "hipMemset(status)"));
+  int rc = refresh_occupancy(h);
+  if (rc != HG_OK) return fail(rc);
+  rc = hg_arm(h, nullptr);
+  if (rc != HG_OK) return fail(rc);
+  e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(hip_fail(e, "hipDeviceSynchronize"));
+  *out = h;
+  return HG_OK;
+}
+
+HG_API int hg_destroy(hg_ctx *h) {
+  if (!h) return HG_OK;
+  int prev = -1;
+  int rc = HG_OK;
+  if (hipGetDevice(&prev) == hipSuccess && prev != h->device) (void)hipSetDevice(h->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) rc = hip_fail(e, "hipDeviceSynchronize");
+  if (h->box) (void)hipFree(h->box);
+  if (h->status) (void)hipFree(h->status);
+  if (prev >= 0 && prev != h->device) (void)hipSetDevice(prev);
+  delete h;
+  return rc;
+}
+
+HG_API int hg_arm(hg_ctx *h, void *stream) {
+  if (!h) return HG_EINVAL;
+  int rc = check_device(h);
+  if (rc != HG_OK) return rc;
+  const long long vectors = 2ll * h->cap * h->vv;
+  const int block = 256;
+  long long grid = (vectors + block - 1) / block;
+  if (grid > static_cast<long long>(h->cus) * 8) grid = static_cast<long long>(h->cus) * 8;
+  HIP_TRY(hg::launch_arm(h->box, vectors, static_cast<int>(grid), block,
+                         static_cast<hipStream_t>(stream)));
+  h->parity = 0;
+  h->pending_m = -1;
+  h->pending_ranks = 0;
+  return HG_OK;
+}
+
+HG_API int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, void *stream) {
+  ShardTable table;
+  int rc = check_call(h, shards, m, h ? all_ranks(h->tp) : 0, false, out, stream, &table);
+  if (rc != HG_OK) return rc;
+  if (!out) return HG_EINVAL;
+  const int vpt = pick_vpt(h, h->tune.fused_vpt, m);
+  const Geometry g = hg::make_geometry(h->tp, h->shard, m, vpt);
+  const int waves = h->tune.fused_block / 64;
+  const long long tiles = (static_cast<long long>(g.chunks) + waves - 1) / waves;
+  const int lim = fused_limit(h, vpt);
+  if (lim < 1) return HG_EINVAL;
+  const int grid = static_cast<int>(tiles < lim ? tiles : lim);
+  HIP_TRY(hg::launch_fused(table, g, vpt, h->tune.push_mode, h->parity_box(h->parity),
+                           static_cast<u32x4 *>(out), h->status, h->poll_limit,
+                           h->tune.poll_skew, grid, h->tune.fused_block,
+                           static_cast<hipStream_t>(stream)));
+  h->parity ^= 1;
+  return HG_OK;
+}
+
+HG_API int hg_push_ranks(hg_ctx *h, const void *const *shards, int m, unsigned long long ranks,
+                         void *stream) {
+  ShardTable table;
+  int rc = check_call(h, shards, m, ranks, true, nullptr, stream, &table);
+  if (rc != HG_OK) return rc;
+  const int vpt = pick_vpt(h, h->tune.split_vpt, m);
+  const Geometry g = hg::make_geometry(h->tp, h->shard, m, vpt);
+  const int block = h->tune.split_block;
+  const int p = h->pending_m >= 0 ? h->pending_parity : h->parity;
+  HIP_TRY(hg::launch_push(table, g, vpt, h->parity_box(p), ranks, split_grid(h, g, block), block,
+                          static_cast<hipStream_t>(stream)));
+  h->pending_m = m;
+  h->pending_parity = p;
+  h->pending_ranks |= ranks;
+  return HG_OK;
+}
+
+HG_API int hg_push(hg_ctx *h, const void *const *shards, int m, void *stream) {
+  if (!h) return HG_EINVAL;
+  if (h->pending_m >= 0) return HG_ESTATE;
+  return hg_push_ranks(h, shards, m, all_ranks(h->tp), stream);
+}
+
+HG_API int hg_collect(hg_ctx *h, int m, void *out, void *stream) {
+  if (!h || m < 0) return HG_EINVAL;
+  if (h->pending_m < 0 || h->pending_m != m) return HG_ESTATE;
+  const int cs = capture_state(static_cast<hipStream_t>(stream));
+  if (cs != HG_OK) return cs;
+  int rc = check_device(h);
+  if (rc != HG_OK) return rc;
+  const size_t out_bytes = static_cast<size_t>(m) * h->row_bytes();
+  const size_t box_bytes = static_cast<size_t>(2) * h->cap * h->row_bytes();
+  if (!out || !aligned16(out) || overlaps(out, out_bytes, h->box, box_bytes)) return HG_EINVAL;
+  const int vpt = pick_vpt(h, h->tune.split_vpt, m);
+  const Geometry g = hg::make_geometry(h->tp, h->shard, m, vpt);
+  const int block = h->tune.split_block;
+  HIP_TRY(hg::launch_collect(g, vpt, h->parity_box(h->pending_parity), static_cast<u32x4 *>(out),
+                             h->status, h->poll_limit, split_grid(h, g, block), block,
+                             static_cast<hipStream_t>(stream)));
+  h->pending_m = -1;
+  h->pending_ranks = 0;
+  h->parity = h->pending_parity ^ 1;
+  return HG_OK;
+}
+
+HG_API int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *out,
+                           void *stream) {
+  if (tp < 1 || tp > HG_MAX_TP || shard < 8 || shard % 8 != 0 || m < 0) return HG_EINVAL;
+  if (m == 0) return HG_OK;
+  if (!out || !aligned16(out)) return HG_EINVAL;
+  const long long vv = static_cast<long long>(tp) * (shard / 8);
+  if (vv * m >= (1ll << 31)) return HG_EINVAL;
+  ShardTable table;
+  const size_t out_bytes = static_cast<size_t>(m) * vv * 16;
+  int rc = load_shards(tp, shard, shards, m, all_ranks(tp), &table, out, out_bytes, nullptr, 0);
+  if (rc != HG_OK) return rc;
+  int dev = 0, cus = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  const int vpt = auto_vpt(m * vv, cus);
+  const Geometry g = hg::make_geometry(tp, shard, m, vpt);
+  const int block = 256;
+  const long long tiles = (static_cast<long long>(g.chunks) + 3) / 4;
+  const long long cap = static_cast<long long>(cus) * 16;
+  HIP_TRY(hg::launch_stock(table, g, vpt, static_cast<u32x4 *>(out),
+                           static_cast<int>(tiles < cap ? tiles : cap), block,
+                           static_cast<hipStream_t>(stream)));
+  return HG_OK;
+}
+
+HG_API int hg_parity(const hg_ctx *h) { return h ? h->parity : HG_EINVAL; }
+
+HG_API int hg_mailbox(const hg_ctx *h, int parity, const void **dev, size_t *bytes) {
+  if (!h || (parity != 0 && parity != 1) || !dev || !bytes) return HG_EINVAL;
+  *dev = h->parity_box(parity);
+  *bytes = static_cast<size_t>(h->cap) * h->row_bytes();
+  return HG_OK;
+}
+
+HG_API int hg_copy_mailbox(const hg_ctx *h, int parity, void *dst, void *stream) {
+  if (!h || (parity != 0 && parity != 1) || !dst) return HG_EINVAL;
+  int rc = check_device(h);
+  if (rc != HG_OK) return rc;
+  const size_t bytes = static_cast<size_t>(h->cap) * h->row_bytes();
+  if (overlaps(dst, bytes, h->box, 2 * bytes)) return HG_EINVAL;
+  HIP_TRY(hipMemcpyAsync(dst, h->parity_box(parity), bytes, hipMemcpyDeviceToDevice,
+                         static_cast<hipStream_t>(stream)));
+  return HG_OK;
+}
+
+HG_API int hg_set_poll_limit(hg_ctx *h, unsigned long long spins) {
+  if (!h) return HG_EINVAL;
+  h->poll_limit = spins ? spins : kDefaultPollLimit;
+  return HG_OK;
+}
+
+HG_API int hg_poll_status(hg_ctx *h, void *stream) {
+  if (!h) return HG_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int cs = capture_state(s);
+  if (cs == HG_EDECLINE) return HG_EINVAL;
+  if (cs != HG_OK) return cs;
+  int rc = check_device(h);
+  if (rc != HG_OK) return rc;
+  unsigned count = 0;
+  HIP_TRY(hipMemcpyAsync(&count, h->status, sizeof count, hipMemcpyDeviceToHost, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  if (count == 0) return HG_OK;
+  HIP_TRY(hipMemsetAsync(h->status, 0, sizeof count, s));
+  HIP_TRY(hipStreamSynchronize(s));
+  return HG_ETIMEOUT;
+}
+
+HG_API int hg_set_tuning(hg_ctx *h, int knob, int value) {
+  if (!h) return HG_EINVAL;
+  switch (knob) {
+    case HG_TUNE_FUSED_BLOCK:
+      if (!valid_block(value)) return HG_EINVAL;
+      h->tune.fused_block = value;
+      return refresh_occupancy(h);
+    case HG_TUNE_FUSED_VPT:
+      if (!valid_vpt(value)) return HG_EINVAL;
+      h->tune.fused_vpt = value;
+      return HG_OK;
+    case HG_TUNE_FUSED_GRID:
+      if (value < 0) return HG_EINVAL;
+      h->tune.fused_grid = value;
+      return HG_OK;
+    case HG_TUNE_SPLIT_BLOCK:
+      if (!valid_block(value)) return HG_EINVAL;
+      h->tune.split_block = value;
+      return HG_OK;
+    case HG_TUNE_SPLIT_VPT:
+      if (!valid_vpt(value)) return HG_EINVAL;
+      h->tune.split_vpt = value;
+      return HG_OK;
+    case HG_TUNE_POLL_SKEW:
+      if (value < 1) return HG_EINVAL;
+      h->tune.poll_skew = value;
+      return HG_OK;
+    case HG_TUNE_PUSH_MODE:
+      if (value != hg::kPushAgentStores && value != hg::kPushPlainFence) return HG_EINVAL;
+      h->tune.push_mode = value;
+      return HG_OK;
+    default:
+      return HG_EINVAL;
+  }
+}
+
+HG_API int hg_get_tuning(const hg_ctx *h, int knob, int *value) {
+  if (!h || !value) return HG_EINVAL;
+  switch (knob) {
+    case HG_TUNE_FUSED_BLOCK: *value = h->tune.fused_block; return HG_OK;
+    case HG_TUNE_FUSED_VPT: *value = h->tune.fused_vpt; return HG_OK;
+    case HG_TUNE_FUSED_GRID: *value = h->tune.fused_grid; return HG_OK;
+    case HG_TUNE_SPLIT_BLOCK: *value = h->tune.split_block; return HG_OK;
+    case HG_TUNE_SPLIT_VPT: *value = h->tune.split_vpt; return HG_OK;
+    case HG_TUNE_POLL_SKEW: *value = h->tune.poll_skew; return HG_OK;
+    case HG_TUNE_PUSH_MODE: *value = h->tune.push_mode; return HG_OK;
+    default: return HG_EINVAL;
+  }
+}
+
+HG_API int hg_fused_grid_limit(const hg_ctx *h) {
+  if (!h) return HG_EINVAL;
+  const int per_cu = h->fused_per_cu[vpt_index(4)][h->tune.push_mode];
+  return per_cu * h->cus;
+}
+
+HG_API const char *hg_strerror(int code) {
+  switch (code) {
+    case HG_OK: return "ok";
+    case HG_EDECLINE: return "declined: take the stock gather";
+    case HG_EINVAL: return "invalid argument";
+    case HG_ENOMEM: return "device memory allocation failed";
+    case HG_EHIP: return "HIP runtime error";
+    case HG_ETIMEOUT: return "a bounded mailbox poll gave up";
+    case HG_ESTATE: return "split push/collect called out of order";
+    default: return "unknown status";
+  }
+}
+
+HG_API const char *hg_last_error_detail(void) { return g_last_error; }

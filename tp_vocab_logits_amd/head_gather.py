@@ -1,0 +1,213 @@
+"""``HeadGather``: the vocab-parallel lm_head's logits gather ``[M, V/TP] x TP
+-> [M, V]`` (BF16) on a two-parity Lamport mailbox, through libhg.so.
+
+Mirrors the gather object on the vLLM API documentation page
+``vllm.models.kimi_k3.nvidia.specialized_decode.runtime.logits_gather``
+(``HeadGather`` class): construction allocates and arms the mailbox; a call
+with a served row count (1..cap) and BF16 shards of the right width, outside
+graph capture, is served by one kernel launch and flips the parity; any other
+call takes the stock gather (rank-order concatenation, bytes unchanged).
+
+Torch provides the device memory and the stream (the current stream of the
+context's device); the wrapper only marshals pointers.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Sequence
+
+import torch
+
+from . import _lib
+from ._lib import HG_EDECLINE, HG_OK, HgError, check, lib, pointer_array
+
+__all__ = ["HeadGather", "HgError", "stock_gather"]
+
+
+def _stream_handle(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shard_pointers(shards, tp: int) -> tuple[list[int], int, int, torch.device, torch.dtype]:
+    """Device pointers of the TP shards (a ``[TP, M, S]`` tensor or a sequence
+    of ``[M, S]`` tensors), plus M, S, the device and the dtype."""
+    if isinstance(shards, torch.Tensor):
+        if shards.dim() != 3 or shards.shape[0] != tp:
+            raise ValueError(f"expected a [TP={tp}, M, S] tensor, got {tuple(shards.shape)}")
+        if not shards.is_contiguous():
+            raise ValueError("the stacked shard tensor must be contiguous")
+        m, s = int(shards.shape[1]), int(shards.shape[2])
+        step = m * s * shards.element_size()
+        base = shards.data_ptr()
+        return [base + r * step for r in range(tp)], m, s, shards.device, shards.dtype
+    shards = list(shards)
+    if len(shards) != tp:
+        raise ValueError(f"expected {tp} shards, got {len(shards)}")
+    m, s = (int(x) for x in shards[0].shape)
+    for t in shards:
+        if t.dim() != 2 or tuple(t.shape) != (m, s) or not t.is_contiguous():
+            raise ValueError("every shard must be a contiguous [M, S] tensor of one shape")
+        if t.dtype != shards[0].dtype or t.device != shards[0].device:
+            raise ValueError("shards must share dtype and device")
+    return [t.data_ptr() for t in shards], m, s, shards[0].device, shards[0].dtype
+
+
+def stock_gather(shards: torch.Tensor | Sequence[torch.Tensor], tp: int,
+                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """The stock gather: rank-order concatenation ``[M, TP*S]``, bytes
+    unchanged (the single-device share of an all-gather followed by the copy to
+    ``[M, V]``). BF16 shards with ``S % 8 == 0`` run in the library's kernel;
+    other dtypes or widths fall to ``torch.cat`` on the shards' device."""
+    ptrs, m, s, device, dtype = _shard_pointers(shards, tp)
+    if out is None:
+        out = torch.empty((m, tp * s), dtype=dtype, device=device)
+    if dtype != torch.bfloat16 or s % 8 or device.type != "cuda":
+        parts = list(shards) if not isinstance(shards, torch.Tensor) else list(shards.unbind(0))
+        torch.cat(parts, dim=1, out=out)
+        return out
+    if m == 0:
+        return out
+    with torch.cuda.device(device):
+        check(lib().hg_stock_gather(tp, s, pointer_array(ptrs), m, ctypes.c_void_p(out.data_ptr()),
+                                    _stream_handle(device)), "hg_stock_gather")
+    return out
+
+
+class HeadGather:
+    """One gather context: ``tp`` virtual ranks of ``shard`` BF16 columns, up to
+    ``cap`` rows per call, on ``device`` (default: the current CUDA device)."""
+
+    def __init__(self, tp: int, shard: int, cap: int, device: torch.device | int | None = None):
+        if device is None:
+            index = torch.cuda.current_device()
+        elif isinstance(device, int):
+            index = device
+        else:
+            d = torch.device(device)
+            index = d.index if d.index is not None else torch.cuda.current_device()
+        self.device = torch.device("cuda", index)
+        self.tp, self.shard, self.cap = int(tp), int(shard), int(cap)
+        self.vocab = self.tp * self.shard
+        self._h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            check(lib().hg_create(self.tp, self.shard, self.cap, ctypes.byref(self._h)), "hg_create")
+
+    # -- lifetime ----------------------------------------------------------
+    def close(self) -> None:
+        if self._h:
+            with torch.cuda.device(self.device):
+                check(lib().hg_destroy(self._h), "hg_destroy")
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- calls -------------------------------------------------------------
+    def _eligible(self, ptrs_m_s_dev_dt) -> bool:
+        _, m, s, device, dtype = ptrs_m_s_dev_dt
+        return dtype == torch.bfloat16 and s == self.shard and device == self.device
+
+    def _out(self, m: int, out: torch.Tensor | None) -> torch.Tensor:
+        if out is None:
+            return torch.empty((m, self.vocab), dtype=torch.bfloat16, device=self.device)
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != (m, self.vocab) or not out.is_contiguous():
+            raise ValueError(f"out must be a contiguous BF16 [{m}, {self.vocab}] tensor")
+        return out
+
+    def __call__(self, shards, out: torch.Tensor | None = None) -> torch.Tensor:
+        """Gather ``[M, S]`` x TP -> ``[M, V]``. Served calls run the fused
+        kernel and flip the parity; declined calls return the stock gather."""
+        info = _shard_pointers(shards, self.tp)
+        ptrs, m = info[0], info[1]
+        if not self._eligible(info):
+            return stock_gather(shards, self.tp, out)
+        out = self._out(m, out)
+        with torch.cuda.device(self.device):
+            rc = lib().hg_gather(self._h, pointer_array(ptrs), m, ctypes.c_void_p(out.data_ptr()),
+                                 _stream_handle(self.device))
+        if rc == HG_EDECLINE:
+            return stock_gather(shards, self.tp, out)
+        check(rc, "hg_gather")
+        return out
+
+    def push(self, shards) -> bool:
+        """Split variant, first half. Returns False when declined."""
+        info = _shard_pointers(shards, self.tp)
+        if not self._eligible(info):
+            return False
+        with torch.cuda.device(self.device):
+            rc = lib().hg_push(self._h, pointer_array(info[0]), info[1], _stream_handle(self.device))
+        return check(rc, "hg_push") == HG_OK
+
+    def push_ranks(self, shards, ranks) -> bool:
+        """Split variant, partial push by the listed ranks only (``shards`` must
+        still hold TP entries; the others are not read). False when declined."""
+        info = _shard_pointers(shards, self.tp)
+        if not self._eligible(info):
+            return False
+        mask = 0
+        for r in ranks:
+            mask |= 1 << int(r)
+        with torch.cuda.device(self.device):
+            rc = lib().hg_push_ranks(self._h, pointer_array(info[0]), info[1], mask,
+                                     _stream_handle(self.device))
+        return check(rc, "hg_push_ranks") == HG_OK
+
+    def collect(self, m: int, out: torch.Tensor | None = None) -> torch.Tensor:
+        """Split variant, second half: the gathered ``[m, V]`` logits."""
+        out = self._out(m, out)
+        with torch.cuda.device(self.device):
+            rc = lib().hg_collect(self._h, m, ctypes.c_void_p(out.data_ptr()),
+                                  _stream_handle(self.device))
+        if rc == HG_EDECLINE:
+            raise HgError(_lib.HG_ESTATE, "hg_collect declined (stream capturing)")
+        check(rc, "hg_collect")
+        return out
+
+    def arm(self) -> None:
+        with torch.cuda.device(self.device):
+            check(lib().hg_arm(self._h, _stream_handle(self.device)), "hg_arm")
+
+    # -- state -------------------------------------------------------------
+    @property
+    def parity(self) -> int:
+        return check(lib().hg_parity(self._h), "hg_parity")
+
+    def mailbox(self, parity: int) -> torch.Tensor:
+        """A copy of one parity of the mailbox as ``[cap, V]`` BF16 (stream-ordered)."""
+        dst = torch.empty((self.cap, self.vocab), dtype=torch.bfloat16, device=self.device)
+        with torch.cuda.device(self.device):
+            check(lib().hg_copy_mailbox(self._h, parity, ctypes.c_void_p(dst.data_ptr()),
+                                        _stream_handle(self.device)), "hg_copy_mailbox")
+        return dst
+
+    def set_poll_limit(self, spins: int) -> None:
+        check(lib().hg_set_poll_limit(self._h, int(spins)), "hg_set_poll_limit")
+
+    def poll_status(self) -> int:
+        """HG_OK, or HG_ETIMEOUT if a bounded poll gave up since the last check."""
+        with torch.cuda.device(self.device):
+            rc = lib().hg_poll_status(self._h, _stream_handle(self.device))
+        if rc == _lib.HG_ETIMEOUT:
+            return rc
+        return check(rc, "hg_poll_status")
+
+    def set_tuning(self, knob: int, value: int) -> None:
+        with torch.cuda.device(self.device):
+            check(lib().hg_set_tuning(self._h, knob, int(value)), "hg_set_tuning")
+
+    def get_tuning(self, knob: int) -> int:
+        v = ctypes.c_int()
+        check(lib().hg_get_tuning(self._h, knob, ctypes.byref(v)), "hg_get_tuning")
+        return v.value
+
+    def fused_grid_limit(self) -> int:
+        return check(lib().hg_fused_grid_limit(self._h), "hg_fused_grid_limit")
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
