@@ -171,17 +171,26 @@ int hg_poll_status(hg_ctx *h, void *stream);
  * built-in choice where noted. */
 #define HG_TUNE_FUSED_BLOCK 1 /* threads per workgroup: 64, 128, 256, 512, 1024          */
 #define HG_TUNE_FUSED_VPT 2   /* 16-byte vectors per lane per chunk: 0 (auto), 1, 2, 4, 8 */
-#define HG_TUNE_FUSED_GRID 3  /* workgroup cap: 0 (co-resident limit) or >= 1            */
+#define HG_TUNE_FUSED_GRID 3  /* workgroup cap: 0 (4 per CU) or >= 1; never above the
+                                 co-resident limit                                      */
 #define HG_TUNE_SPLIT_BLOCK 4 /* as HG_TUNE_FUSED_BLOCK, for push / collect / stock      */
 #define HG_TUNE_SPLIT_VPT 5   /* as HG_TUNE_FUSED_VPT, for push / collect / stock        */
-#define HG_TUNE_POLL_SKEW 6   /* fused: workgroup b polls what b-skew pushed; >= 1       */
-#define HG_TUNE_PUSH_MODE 7   /* 0: agent-coherent stores; 1: plain stores + release fence */
+#define HG_TUNE_POLL_SKEW 6   /* fused: workgroup b polls what (b-skew) mod grid pushed; 0: its own */
+#define HG_TUNE_PUSH_MODE 7   /* fused push: 0 two 64-bit agent-scope atomic stores;
+                                 1 plain 128-bit stores + an agent-scope release fence;
+                                 2 128-bit stores, agent-coherent (sc1) policy;
+                                 3 as 2 with the non-temporal hint                      */
+#define HG_TUNE_POLL_MODE 8   /* poll: 0 two 64-bit agent-scope atomic loads;
+                                 1 128-bit loads, agent-coherent (sc1) policy;
+                                 2 as 1 with the non-temporal hint                      */
+#define HG_TUNE_REARM_MODE 9  /* re-arm stores: 0 plain, 1 non-temporal                 */
 int hg_set_tuning(hg_ctx *h, int knob, int value);
 int hg_get_tuning(const hg_ctx *h, int knob, int *value);
 
-/* Workgroups the fused kernel may keep resident at once on the context's
- * device with the current block size (the grid cap), or a negative code. */
-int hg_fused_grid_limit(const hg_ctx *h);
+/* Workgroups the fused kernel of an m-row call may keep resident at once on
+ * the context's device with the current launch knobs (the grid cap), or a
+ * negative code. */
+int hg_fused_grid_limit(hg_ctx *h, int m);
 
 /* Static description of a status code. */
 const char *hg_strerror(int code);

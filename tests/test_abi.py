@@ -73,7 +73,7 @@ def test_null_context_paths():
     assert lib.hg_set_tuning(null, _lib.TUNE_FUSED_BLOCK, 256) == _lib.HG_EINVAL
     v = ctypes.c_int()
     assert lib.hg_get_tuning(null, _lib.TUNE_FUSED_BLOCK, ctypes.byref(v)) == _lib.HG_EINVAL
-    assert lib.hg_fused_grid_limit(null) == _lib.HG_EINVAL
+    assert lib.hg_fused_grid_limit(null, 1) == _lib.HG_EINVAL
 
 
 def test_stock_gather_argument_checks():

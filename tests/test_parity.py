@@ -102,10 +102,15 @@ GEOMETRIES = [(2, 8, 3), (3, 24, 3), (8, 8, 2), (5, 520, 3), (8, 2056, 3), (2, 4
               (4, 64 * 8 * 8, 2), (64, 16, 2)]
 
 
+# (push, poll, re-arm) flavours of the kernels
+MODES = [(0, 0, 0), (2, 1, 1), (3, 2, 0), (1, 1, 1)]
+
+
+@pytest.mark.parametrize("modes", MODES, ids=lambda m: "push%d-poll%d-rearm%d" % m)
 @pytest.mark.parametrize("vpt", [1, 2, 4, 8])
 @pytest.mark.parametrize("tp,shard,cap", GEOMETRIES)
-def test_ragged_geometries_all_vpt(tp, shard, cap, vpt):
-    note(f"ragged tp={tp} shard={shard} cap={cap} vpt={vpt}")
+def test_ragged_geometries_all_vpt(tp, shard, cap, vpt, modes):
+    note(f"ragged tp={tp} shard={shard} cap={cap} vpt={vpt} modes={modes}")
     w = syn.WORKLOADS["spec"]
     ms = [1, cap, max(1, cap - 1), cap, 1]
     sets = []
@@ -114,7 +119,8 @@ def test_ragged_geometries_all_vpt(tp, shard, cap, vpt):
         syn.inject_sentinel_words(s, 0.03, 99 + i)
         sets.append(s)
     for variant in ("fused", "split"):
-        hg = make(tp, shard, cap, fused_vpt=vpt, split_vpt=vpt)
+        hg = make(tp, shard, cap, fused_vpt=vpt, split_vpt=vpt, push_mode=modes[0],
+                  poll_mode=modes[1], rearm_mode=modes[2])
         sim = og.MailboxSim(tp, shard, cap)
         for n, s in enumerate(sets):
             if variant == "fused":
@@ -129,15 +135,18 @@ def test_ragged_geometries_all_vpt(tp, shard, cap, vpt):
 
 
 @pytest.mark.parametrize("block", [64, 256, 1024])
-@pytest.mark.parametrize("mode", [0, 1])
-@pytest.mark.parametrize("grid,skew", [(0, 1), (1, 1), (3, 1), (7, 2), (0, 3), (0, 100000)])
-def test_fused_launch_shapes(block, mode, grid, skew):
+@pytest.mark.parametrize("push,poll", [(p, q) for p in range(4) for q in range(3)])
+@pytest.mark.parametrize("grid,skew", [(0, 1), (1, 1), (3, 1), (7, 2), (0, 3), (7, 7), (5, 100000),
+                                       (0, 0)])
+def test_fused_launch_shapes(block, push, poll, grid, skew):
     """Every poll ownership: grid 1 (one workgroup polls its own pushes), small
-    grids with many tiles per workgroup, skews that cross workgroups and XCDs,
-    and both ways of publishing the push."""
-    note(f"fused shapes block={block} mode={mode} grid={grid} skew={skew}")
+    grids with many tiles per workgroup, skews that cross workgroups and XCDs
+    (a skew that is a multiple of the grid makes every workgroup poll its own
+    pushes), and both ways of publishing the push."""
+    note(f"fused shapes block={block} push={push} poll={poll} grid={grid} skew={skew}")
     tp, shard, cap = 8, 2048, 4
-    hg = make(tp, shard, cap, fused_block=block, push_mode=mode, fused_grid=grid, poll_skew=skew)
+    hg = make(tp, shard, cap, fused_block=block, push_mode=push, poll_mode=poll, fused_grid=grid,
+              poll_skew=skew, rearm_mode=(push + poll) % 2)
     sim = og.MailboxSim(tp, shard, cap)
     w = syn.WORKLOADS["spec"]
     sets = [syn.shard_set(w, k, rows=m, tp=tp, shard=shard) for k, m in enumerate([4, 1, 3, 4])]

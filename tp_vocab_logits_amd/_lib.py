@@ -31,6 +31,8 @@ TUNE_SPLIT_BLOCK = 4
 TUNE_SPLIT_VPT = 5
 TUNE_POLL_SKEW = 6
 TUNE_PUSH_MODE = 7
+TUNE_POLL_MODE = 8
+TUNE_REARM_MODE = 9
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -55,7 +57,7 @@ SIGNATURES = {
     "hg_poll_status": (_i, [_ctxp, _vp]),
     "hg_set_tuning": (_i, [_ctxp, _i, _i]),
     "hg_get_tuning": (_i, [_ctxp, _i, ctypes.POINTER(_i)]),
-    "hg_fused_grid_limit": (_i, [_ctxp]),
+    "hg_fused_grid_limit": (_i, [_ctxp, _i]),
     "hg_strerror": (ctypes.c_char_p, [_i]),
     "hg_last_error_detail": (ctypes.c_char_p, []),
 }

@@ -16,9 +16,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr uint32_t kSentinel = 0x80000000u;
 
 // Rank r's shard block: [m][shard] BF16, contiguous rows, 16-byte aligned.
-struct ShardTable {
-  const u32x4 *p[HG_MAX_TP];
+// Passed by value in the kernel arguments; launches for up to 8 ranks use an
+// 8-entry copy, since every kernel-argument byte is written by the host at
+// launch (a 64-entry table costs about a microsecond of launch time).
+template <int N>
+struct ShardTableN {
+  const u32x4 *p[N];
 };
+using ShardTable = ShardTableN<HG_MAX_TP>;
+constexpr int kSmallTable = 8;
 
 // Work geometry of one launch. Work is cut into wave-sized chunks: a chunk is
 // 64 * vpt consecutive vectors of one (row, rank) segment, so the rank -- and
@@ -31,29 +37,50 @@ struct Geometry {
   int chunks;  // m * tp * cps
 };
 
-// How the push makes its mailbox stores visible to pollers in other
+// How the fused push makes its mailbox stores visible to pollers in other
 // workgroups of the same kernel.
 enum PushMode : int {
-  kPushAgentStores = 0,  // relaxed agent-scope atomic stores
-  kPushPlainFence = 1,   // plain stores, one agent-scope release fence per wave
+  kPushAgent64 = 0,    // 2 x 64-bit relaxed agent-scope atomic stores
+  kPushPlain = 1,      // plain 128-bit stores, one agent-scope release fence per wave
+  kPushB128Sc1 = 2,    // 128-bit stores with the agent-coherence (sc1) cache policy
+  kPushB128Sc1Nt = 3,  // the same with the non-temporal hint
+  kPushStream = 4,     // 128-bit non-temporal stores, visible at kernel end (split push)
+};
+
+// How a poll reads the mailbox.
+enum PollMode : int {
+  kPollAgent64 = 0,    // 2 x 64-bit relaxed agent-scope atomic loads
+  kPollB128Sc1 = 1,    // 128-bit loads with the agent-coherence (sc1) cache policy
+  kPollB128Sc1Nt = 2,  // the same with the non-temporal hint
+};
+
+// Kernel variant of one launch.
+struct Modes {
+  int vpt;           // 16-byte vectors per lane per chunk: 1, 2, 4, 8
+  int push;          // PushMode (fused kernel)
+  int poll;          // PollMode
+  int rearm_stream;  // re-arm with non-temporal stores (1) or plain stores (0)
 };
 
 // Builds the geometry for m rows at `vpt` vectors per lane.
 Geometry make_geometry(int tp, int shard, int m, int vpt);
 
 // Kernel launchers. Each returns the launch status (hipGetLastError).
+// `box_bytes` is the size of the mailbox rows in use from `box` on (it bounds
+// the 128-bit coherent accesses, which use 32-bit offsets).
 hipError_t launch_arm(u32x4 *box, long long vectors, int grid, int block, hipStream_t s);
-hipError_t launch_fused(const ShardTable &sh, const Geometry &g, int vpt, int mode, u32x4 *box,
-                        u32x4 *out, unsigned *status, unsigned long long limit, int skew,
-                        int grid, int block, hipStream_t s);
+hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md, u32x4 *box,
+                        unsigned box_bytes, u32x4 *out, unsigned *status, unsigned long long limit,
+                        int skew, int grid, int block, hipStream_t s);
 hipError_t launch_push(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *box,
                        unsigned long long ranks, int grid, int block, hipStream_t s);
-hipError_t launch_collect(const Geometry &g, int vpt, u32x4 *box, u32x4 *out, unsigned *status,
-                          unsigned long long limit, int grid, int block, hipStream_t s);
+hipError_t launch_collect(const Geometry &g, const Modes &md, u32x4 *box, unsigned box_bytes,
+                          u32x4 *out, unsigned *status, unsigned long long limit, int grid,
+                          int block, hipStream_t s);
 hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *out, int grid,
                         int block, hipStream_t s);
 
-// Resident workgroups per CU for a kernel instantiation and block size.
-hipError_t fused_blocks_per_cu(int vpt, int mode, int block, int *blocks);
+// Resident workgroups per CU of the fused kernel variant at a block size.
+hipError_t fused_blocks_per_cu(const Modes &md, int tp, int block, int *blocks);
 
 }  // namespace hg

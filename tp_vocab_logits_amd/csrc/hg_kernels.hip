@@ -15,6 +15,16 @@
 // segment; wave w of a workgroup takes chunk `tile * waves + w`. Because the
 // rank is uniform over the wave, the shard pointer is read with one scalar load
 // from the kernel-argument table.
+//
+// Visibility inside one kernel. The eight XCDs of an MI355X each have their
+// own L2, so a mailbox word pushed by one workgroup reaches a poller on another
+// XCD only through memory-side caches or HBM. Pushes therefore use stores with
+// agent scope -- relaxed 64-bit atomics, or 128-bit stores carrying the same
+// `sc1` cache-policy bit the compiler gives agent-scope atomics -- or plain
+// stores followed by one agent-scope release fence; polls use loads with agent
+// scope (64-bit relaxed atomics or 128-bit `sc1` loads), so a re-read never
+// returns a stale line of the poller's own L1 or L2. Every 32-bit word is
+// written and read whole, and the poll tests every word of a vector.
 
 #include "hg_internal.h"
 
@@ -24,6 +34,12 @@ namespace {
 
 constexpr int kWave = 64;
 
+// Buffer-resource word 3 for raw 32-bit data on the gfx9 family (gfx950).
+constexpr int kRawBufferWord3 = 0x00020000;
+// Cache-policy operand of the buffer intrinsics on gfx94x/gfx950.
+constexpr int kPolicySc1 = 16;
+constexpr int kPolicyNt = 2;
+
 __device__ __forceinline__ u32x4 load_stream(const u32x4 *p) {
   return __builtin_nontemporal_load(p);
 }
@@ -32,11 +48,10 @@ __device__ __forceinline__ void store_stream(u32x4 *p, u32x4 v) {
   __builtin_nontemporal_store(v, p);
 }
 
-// Agent-coherent read of one vector: two relaxed 64-bit atomic loads at agent
-// scope, so a re-read is never served from a stale cache line of this CU or
-// this XCD. Each 32-bit word is read atomically; the four words of a vector
-// may be read at different moments, which is why every word is tested.
-__device__ __forceinline__ u32x4 load_agent(const u32x4 *p) {
+// Two relaxed 64-bit atomic loads at agent scope. Each 32-bit word is read
+// atomically; the four words of a vector may be read at different moments,
+// which is why every word is tested.
+__device__ __forceinline__ u32x4 load_agent64(const u32x4 *p) {
   uint64_t *q = reinterpret_cast<uint64_t *>(const_cast<u32x4 *>(p));
   const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -44,10 +59,8 @@ __device__ __forceinline__ u32x4 load_agent(const u32x4 *p) {
                static_cast<uint32_t>(b >> 32)};
 }
 
-// Agent-coherent write of one vector: two relaxed 64-bit atomic stores at
-// agent scope (visible to agent-scope loads of other workgroups without a
-// fence).
-__device__ __forceinline__ void store_agent(u32x4 *p, u32x4 v) {
+// Two relaxed 64-bit atomic stores at agent scope.
+__device__ __forceinline__ void store_agent64(u32x4 *p, u32x4 v) {
   uint64_t *q = reinterpret_cast<uint64_t *>(p);
   __hip_atomic_store(q, static_cast<uint64_t>(v.x) | (static_cast<uint64_t>(v.y) << 32),
                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -65,6 +78,52 @@ __device__ __forceinline__ u32x4 rewrite_sentinel(u32x4 v) {
 
 __device__ __forceinline__ bool has_sentinel(u32x4 v) {
   return (v.x == kSentinel) | (v.y == kSentinel) | (v.z == kSentinel) | (v.w == kSentinel);
+}
+
+// The mailbox rows of one call, as a pointer and as a buffer resource
+// (base = row 0 of the parity, size = the rows in use; used by the 128-bit
+// coherent flavours, whose offsets are 32-bit).
+struct Box {
+  u32x4 *ptr;
+  __amdgpu_buffer_rsrc_t rsrc;
+};
+
+__device__ __forceinline__ Box make_box(u32x4 *ptr, unsigned bytes) {
+  return Box{ptr, __builtin_amdgcn_make_buffer_rsrc(ptr, 0, static_cast<int>(bytes),
+                                                    kRawBufferWord3)};
+}
+
+// A pointer-only view (stores through `ptr`; the resource is never used).
+__device__ __forceinline__ Box pointer_box(u32x4 *ptr) {
+  return Box{ptr, __builtin_amdgcn_make_buffer_rsrc(ptr, 0, 0, kRawBufferWord3)};
+}
+
+template <int STORE>
+__device__ __forceinline__ void box_store(const Box &b, long long idx, u32x4 v) {
+  if constexpr (STORE == kPushAgent64) {
+    store_agent64(b.ptr + idx, v);
+  } else if constexpr (STORE == kPushPlain) {
+    b.ptr[idx] = v;
+  } else if constexpr (STORE == kPushB128Sc1) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, b.rsrc, static_cast<int>(idx * 16), 0, kPolicySc1);
+  } else if constexpr (STORE == kPushB128Sc1Nt) {
+    __builtin_amdgcn_raw_buffer_store_b128(v, b.rsrc, static_cast<int>(idx * 16), 0,
+                                           kPolicySc1 | kPolicyNt);
+  } else {
+    store_stream(b.ptr + idx, v);
+  }
+}
+
+template <int POLL>
+__device__ __forceinline__ u32x4 box_load(const Box &b, long long idx) {
+  if constexpr (POLL == kPollAgent64) {
+    return load_agent64(b.ptr + idx);
+  } else if constexpr (POLL == kPollB128Sc1) {
+    return __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, static_cast<int>(idx * 16), 0, kPolicySc1);
+  } else {
+    return __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, static_cast<int>(idx * 16), 0,
+                                                 kPolicySc1 | kPolicyNt);
+  }
 }
 
 struct ChunkPos {
@@ -87,43 +146,30 @@ __device__ __forceinline__ ChunkPos chunk_pos(int c, const Geometry &g, int vpt)
   return p;
 }
 
-// Store flavours for the push / copy side.
-enum Store : int { kStoreAgent = 0, kStorePlain = 1, kStoreStream = 2 };
-
 // Push one chunk: read the shard vectors, rewrite sentinel words (REWRITE),
 // store them at the segment's place in `dst` ([m][vv] vectors). A full chunk
 // (the wave-uniform common case) runs without per-lane bounds tests, so the
 // compiler keeps loads of the next chunk free of waits on this one's stores.
-template <int STORE>
-__device__ __forceinline__ void store_vec(u32x4 *p, u32x4 w) {
-  if (STORE == kStoreAgent) {
-    store_agent(p, w);
-  } else if (STORE == kStorePlain) {
-    *p = w;
-  } else {
-    store_stream(p, w);
-  }
-}
-
-template <int VPT, bool REWRITE, int STORE>
-__device__ __forceinline__ void push_chunk(const ShardTable &sh, const Geometry &g, int c, int lane,
-                                           u32x4 *dst) {
+template <int VPT, bool REWRITE, int STORE, class Table>
+__device__ __forceinline__ void push_chunk(const Table &sh, const Geometry &g, int c, int lane,
+                                           const Box &dst) {
   const ChunkPos p = chunk_pos(c, g, VPT);
   const u32x4 *src = sh.p[p.rank] + static_cast<long long>(p.row) * g.sv + p.k0 + lane;
-  u32x4 *d = dst + p.base + p.k0 + lane;
+  const long long d = p.base + p.k0 + lane;
   if (p.k0 + kWave * VPT <= g.sv) {
     u32x4 v[VPT];
 #pragma unroll
     for (int i = 0; i < VPT; ++i) v[i] = load_stream(src + i * kWave);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) store_vec<STORE>(d + i * kWave, REWRITE ? rewrite_sentinel(v[i]) : v[i]);
+    for (int i = 0; i < VPT; ++i)
+      box_store<STORE>(dst, d + i * kWave, REWRITE ? rewrite_sentinel(v[i]) : v[i]);
   } else {
     const int left = g.sv - p.k0 - lane;  // vectors of this segment from this lane on
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       if (i * kWave < left) {
         const u32x4 v = load_stream(src + i * kWave);
-        store_vec<STORE>(d + i * kWave, REWRITE ? rewrite_sentinel(v) : v);
+        box_store<STORE>(dst, d + i * kWave, REWRITE ? rewrite_sentinel(v) : v);
       }
     }
   }
@@ -138,48 +184,59 @@ struct PollBudget {
 
 // Re-read one vector until none of its words is the sentinel, within the
 // lane's budget.
-__device__ __forceinline__ u32x4 await_vec(const u32x4 *p, u32x4 v, unsigned *status,
-                                           PollBudget &b) {
-  while (!b.gave_up && has_sentinel(v)) {
-    if (++b.spins > b.limit) {
-      b.gave_up = true;
+template <int POLL>
+__device__ __forceinline__ u32x4 await_vec(const Box &b, long long idx, u32x4 v, unsigned *status,
+                                           PollBudget &bud) {
+  while (!bud.gave_up && has_sentinel(v)) {
+    if (++bud.spins > bud.limit) {
+      bud.gave_up = true;
       __hip_atomic_fetch_add(status, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     __builtin_amdgcn_s_sleep(1);
-    v = load_agent(p);
+    __asm__ __volatile__("" ::: "memory");  // the re-read is a new read
+    v = box_load<POLL>(b, idx);
   }
   return v;
 }
 
+__device__ __forceinline__ void rearm_store(const Box &b, long long idx, bool stream) {
+  const u32x4 armed = {kSentinel, kSentinel, kSentinel, kSentinel};
+  if (stream)
+    store_stream(b.ptr + idx, armed);
+  else
+    b.ptr[idx] = armed;
+}
+
 // Poll one chunk of the mailbox until no word is the sentinel, copy it to
 // `out` and re-arm it.
-template <int VPT>
-__device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane, u32x4 *box,
-                                              u32x4 *out, unsigned *status, PollBudget &b) {
+template <int VPT, int POLL>
+__device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane, const Box &box,
+                                              u32x4 *out, unsigned *status, PollBudget &bud,
+                                              bool rearm_stream) {
   const ChunkPos p = chunk_pos(c, g, VPT);
-  u32x4 *bx = box + p.base + p.k0 + lane;
-  u32x4 *o = out + p.base + p.k0 + lane;
-  const u32x4 armed = {kSentinel, kSentinel, kSentinel, kSentinel};
+  const long long d = p.base + p.k0 + lane;
+  u32x4 *o = out + d;
   if (p.k0 + kWave * VPT <= g.sv) {
     u32x4 v[VPT];
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) v[i] = load_agent(bx + i * kWave);
+    for (int i = 0; i < VPT; ++i) v[i] = box_load<POLL>(box, d + i * kWave);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) v[i] = await_vec(bx + i * kWave, v[i], status, b);
+    for (int i = 0; i < VPT; ++i) v[i] = await_vec<POLL>(box, d + i * kWave, v[i], status, bud);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       store_stream(o + i * kWave, v[i]);
-      bx[i * kWave] = armed;
+      rearm_store(box, d + i * kWave, rearm_stream);
     }
   } else {
     const int left = g.sv - p.k0 - lane;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       if (i * kWave < left) {
-        const u32x4 v = await_vec(bx + i * kWave, load_agent(bx + i * kWave), status, b);
+        const long long idx = d + i * kWave;
+        const u32x4 v = await_vec<POLL>(box, idx, box_load<POLL>(box, idx), status, bud);
         store_stream(o + i * kWave, v);
-        bx[i * kWave] = armed;
+        rearm_store(box, idx, rearm_stream);
       }
     }
   }
@@ -207,89 +264,134 @@ __global__ __launch_bounds__(1024) void k_arm(u32x4 *box, long long vectors) {
 
 // One launch does the whole gather. Phase 1: workgroup b pushes tiles
 // b, b+G, b+2G, ... Phase 2: it polls, copies and re-arms the tiles pushed by
-// workgroup b-skew (its own for b < skew). Every wait is thus on a workgroup
-// with a lower index, which the dispatcher started earlier and whose push
-// never waits on anything; the grid is also capped at the co-resident limit.
-template <int VPT, int MODE>
-__global__ __launch_bounds__(1024) void k_fused(ShardTable sh, Geometry g, u32x4 *box, u32x4 *out,
-                                                unsigned *status, unsigned long long limit,
-                                                int skew) {
+// workgroup (b - skew) mod G, a rotation, so every tile is collected exactly
+// once and, with skew 1, by a workgroup on another XCD (workgroups are dealt
+// to the XCDs round-robin); skew 0 collects its own tiles. No workgroup waits
+// before its own push is done, and the grid is capped at the co-resident
+// limit, so every workgroup whose pushes are awaited is running. Beyond that,
+// only the first `skew` workgroups wait on a higher-numbered one; every other
+// wait is on a workgroup dispatched earlier.
+template <int VPT, int PUSH, int POLL, int NT>
+__global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, u32x4 *box_ptr,
+                                                unsigned box_bytes, u32x4 *out, unsigned *status,
+                                                unsigned long long limit, int skew,
+                                                int rearm_stream) {
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
   const int tiles = (g.chunks + waves - 1) / waves;
   const int grid = static_cast<int>(gridDim.x);
   const int me = static_cast<int>(blockIdx.x);
+  const Box box = make_box(box_ptr, box_bytes);
 
   for (int t = me; t < tiles; t += grid) {
     const int c = t * waves + wave;
-    if (c < g.chunks)
-      push_chunk<VPT, true, MODE == kPushAgentStores ? kStoreAgent : kStorePlain>(sh, g, c, lane,
-                                                                                   box);
+    if (c < g.chunks) push_chunk<VPT, true, PUSH>(sh, g, c, lane, box);
   }
-  if (MODE == kPushPlainFence) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if constexpr (PUSH == kPushPlain) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 
-  PollBudget b{0ull, limit, false};
-  const int from = me >= skew ? me - skew : me;
+  PollBudget bud{0ull, limit, false};
+  const int from =
+      skew == 0 ? me : static_cast<int>(((static_cast<long long>(me) - skew) % grid + grid) % grid);
   for (int t = from; t < tiles; t += grid) {
     const int c = t * waves + wave;
-    if (c < g.chunks) collect_chunk<VPT>(g, c, lane, box, out, status, b);
+    if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud, rearm_stream);
   }
 }
 
 // Split variant, first half: the push alone, by the ranks whose bit is set in
 // `ranks` (visible to the next kernel on the stream at kernel end).
-template <int VPT>
-__global__ __launch_bounds__(1024) void k_push(ShardTable sh, Geometry g, u32x4 *box,
+template <int VPT, int NT>
+__global__ __launch_bounds__(1024) void k_push(ShardTableN<NT> sh, Geometry g, u32x4 *box_ptr,
                                                unsigned long long ranks) {
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
   const int tiles = (g.chunks + waves - 1) / waves;
+  const Box box = pointer_box(box_ptr);
   for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
     const int c = t * waves + wave;
     if (c >= g.chunks) continue;
     const int rank = (c / g.cps) % g.tp;
-    if ((ranks >> rank) & 1ull) push_chunk<VPT, true, kStoreStream>(sh, g, c, lane, box);
+    if ((ranks >> rank) & 1ull) push_chunk<VPT, true, kPushStream>(sh, g, c, lane, box);
   }
 }
 
 // Split variant, second half: poll, copy, re-arm.
-template <int VPT>
-__global__ __launch_bounds__(1024) void k_collect(Geometry g, u32x4 *box, u32x4 *out,
-                                                  unsigned *status, unsigned long long limit) {
+template <int VPT, int POLL>
+__global__ __launch_bounds__(1024) void k_collect(Geometry g, u32x4 *box_ptr, unsigned box_bytes,
+                                                  u32x4 *out, unsigned *status,
+                                                  unsigned long long limit, int rearm_stream) {
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
   const int tiles = (g.chunks + waves - 1) / waves;
-  PollBudget b{0ull, limit, false};
+  const Box box = make_box(box_ptr, box_bytes);
+  PollBudget bud{0ull, limit, false};
   for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
     const int c = t * waves + wave;
-    if (c < g.chunks) collect_chunk<VPT>(g, c, lane, box, out, status, b);
+    if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud, rearm_stream);
   }
 }
 
 // The stock path's single-device share: rank-order concatenation, bytes
 // unchanged.
-template <int VPT>
-__global__ __launch_bounds__(1024) void k_stock(ShardTable sh, Geometry g, u32x4 *out) {
+template <int VPT, int NT>
+__global__ __launch_bounds__(1024) void k_stock(ShardTableN<NT> sh, Geometry g, u32x4 *out) {
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
   const int tiles = (g.chunks + waves - 1) / waves;
+  const Box dst = pointer_box(out);
   for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
     const int c = t * waves + wave;
-    if (c < g.chunks) push_chunk<VPT, false, kStoreStream>(sh, g, c, lane, out);
+    if (c < g.chunks) push_chunk<VPT, false, kPushStream>(sh, g, c, lane, dst);
   }
 }
+
+template <int N>
+using Int = std::integral_constant<int, N>;
 
 template <typename F>
 hipError_t by_vpt(int vpt, F &&f) {
   switch (vpt) {
-    case 1: return f(std::integral_constant<int, 1>{});
-    case 2: return f(std::integral_constant<int, 2>{});
-    case 4: return f(std::integral_constant<int, 4>{});
-    case 8: return f(std::integral_constant<int, 8>{});
+    case 1: return f(Int<1>{});
+    case 2: return f(Int<2>{});
+    case 4: return f(Int<4>{});
+    case 8: return f(Int<8>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Calls f with the shard table in its launch form: an 8-entry copy for up to
+// 8 ranks, the full table otherwise.
+template <typename F>
+hipError_t by_table(const ShardTable &sh, int tp, F &&f) {
+  if (tp <= kSmallTable) {
+    ShardTableN<kSmallTable> t;
+    for (int r = 0; r < kSmallTable; ++r) t.p[r] = sh.p[r];
+    return f(t);
+  }
+  return f(sh);
+}
+
+template <typename F>
+hipError_t by_push(int mode, F &&f) {
+  switch (mode) {
+    case kPushAgent64: return f(Int<kPushAgent64>{});
+    case kPushPlain: return f(Int<kPushPlain>{});
+    case kPushB128Sc1: return f(Int<kPushB128Sc1>{});
+    case kPushB128Sc1Nt: return f(Int<kPushB128Sc1Nt>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename F>
+hipError_t by_poll(int mode, F &&f) {
+  switch (mode) {
+    case kPollAgent64: return f(Int<kPollAgent64>{});
+    case kPollB128Sc1: return f(Int<kPollB128Sc1>{});
+    case kPollB128Sc1Nt: return f(Int<kPollB128Sc1Nt>{});
     default: return hipErrorInvalidValue;
   }
 }
@@ -312,55 +414,72 @@ hipError_t launch_arm(u32x4 *box, long long vectors, int grid, int block, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_fused(const ShardTable &sh, const Geometry &g, int vpt, int mode, u32x4 *box,
-                        u32x4 *out, unsigned *status, unsigned long long limit, int skew,
-                        int grid, int block, hipStream_t s) {
-  return by_vpt(vpt, [&](auto v) {
-    constexpr int V = decltype(v)::value;
-    if (mode == kPushPlainFence)
-      hipLaunchKernelGGL((k_fused<V, kPushPlainFence>), dim3(grid), dim3(block), 0, s, sh, g, box,
-                         out, status, limit, skew);
-    else
-      hipLaunchKernelGGL((k_fused<V, kPushAgentStores>), dim3(grid), dim3(block), 0, s, sh, g,
-                         box, out, status, limit, skew);
-    return hipGetLastError();
+hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md, u32x4 *box,
+                        unsigned box_bytes, u32x4 *out, unsigned *status, unsigned long long limit,
+                        int skew, int grid, int block, hipStream_t s) {
+  return by_table(sh, g.tp, [&](const auto &t) {
+    constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
+    return by_vpt(md.vpt, [&](auto v) {
+      return by_push(md.push, [&](auto pu) {
+        return by_poll(md.poll, [&](auto po) {
+          constexpr int V = decltype(v)::value, PU = decltype(pu)::value, PO = decltype(po)::value;
+          hipLaunchKernelGGL((k_fused<V, PU, PO, NT>), dim3(grid), dim3(block), 0, s, t, g, box,
+                             box_bytes, out, status, limit, skew, md.rearm_stream);
+          return hipGetLastError();
+        });
+      });
+    });
   });
 }
 
 hipError_t launch_push(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *box,
                        unsigned long long ranks, int grid, int block, hipStream_t s) {
-  return by_vpt(vpt, [&](auto v) {
-    constexpr int V = decltype(v)::value;
-    hipLaunchKernelGGL((k_push<V>), dim3(grid), dim3(block), 0, s, sh, g, box, ranks);
-    return hipGetLastError();
+  return by_table(sh, g.tp, [&](const auto &t) {
+    constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
+    return by_vpt(vpt, [&](auto v) {
+      constexpr int V = decltype(v)::value;
+      hipLaunchKernelGGL((k_push<V, NT>), dim3(grid), dim3(block), 0, s, t, g, box, ranks);
+      return hipGetLastError();
+    });
   });
 }
 
-hipError_t launch_collect(const Geometry &g, int vpt, u32x4 *box, u32x4 *out, unsigned *status,
-                          unsigned long long limit, int grid, int block, hipStream_t s) {
-  return by_vpt(vpt, [&](auto v) {
-    constexpr int V = decltype(v)::value;
-    hipLaunchKernelGGL((k_collect<V>), dim3(grid), dim3(block), 0, s, g, box, out, status, limit);
-    return hipGetLastError();
+hipError_t launch_collect(const Geometry &g, const Modes &md, u32x4 *box, unsigned box_bytes,
+                          u32x4 *out, unsigned *status, unsigned long long limit, int grid,
+                          int block, hipStream_t s) {
+  return by_vpt(md.vpt, [&](auto v) {
+    return by_poll(md.poll, [&](auto po) {
+      constexpr int V = decltype(v)::value, PO = decltype(po)::value;
+      hipLaunchKernelGGL((k_collect<V, PO>), dim3(grid), dim3(block), 0, s, g, box, box_bytes, out,
+                         status, limit, md.rearm_stream);
+      return hipGetLastError();
+    });
   });
 }
 
 hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *out, int grid,
                         int block, hipStream_t s) {
-  return by_vpt(vpt, [&](auto v) {
-    constexpr int V = decltype(v)::value;
-    hipLaunchKernelGGL((k_stock<V>), dim3(grid), dim3(block), 0, s, sh, g, out);
-    return hipGetLastError();
+  return by_table(sh, g.tp, [&](const auto &t) {
+    constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
+    return by_vpt(vpt, [&](auto v) {
+      constexpr int V = decltype(v)::value;
+      hipLaunchKernelGGL((k_stock<V, NT>), dim3(grid), dim3(block), 0, s, t, g, out);
+      return hipGetLastError();
+    });
   });
 }
 
-hipError_t fused_blocks_per_cu(int vpt, int mode, int block, int *blocks) {
-  return by_vpt(vpt, [&](auto v) {
-    constexpr int V = decltype(v)::value;
-    const void *fn = mode == kPushPlainFence
-                         ? reinterpret_cast<const void *>(&k_fused<V, kPushPlainFence>)
-                         : reinterpret_cast<const void *>(&k_fused<V, kPushAgentStores>);
-    return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fn, block, 0);
+hipError_t fused_blocks_per_cu(const Modes &md, int tp, int block, int *blocks) {
+  return by_vpt(md.vpt, [&](auto v) {
+    return by_push(md.push, [&](auto pu) {
+      return by_poll(md.poll, [&](auto po) {
+        constexpr int V = decltype(v)::value, PU = decltype(pu)::value, PO = decltype(po)::value;
+        const void *fn = tp <= kSmallTable
+                             ? reinterpret_cast<const void *>(&k_fused<V, PU, PO, kSmallTable>)
+                             : reinterpret_cast<const void *>(&k_fused<V, PU, PO, HG_MAX_TP>);
+        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fn, block, 0);
+      });
+    });
   });
 }
 

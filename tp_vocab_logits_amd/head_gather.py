@@ -205,8 +205,9 @@ class HeadGather:
         check(lib().hg_get_tuning(self._h, knob, ctypes.byref(v)), "hg_get_tuning")
         return v.value
 
-    def fused_grid_limit(self) -> int:
-        return check(lib().hg_fused_grid_limit(self._h), "hg_fused_grid_limit")
+    def fused_grid_limit(self, m: int) -> int:
+        with torch.cuda.device(self.device):
+            return check(lib().hg_fused_grid_limit(self._h, int(m)), "hg_fused_grid_limit")
 
     @property
     def handle(self) -> ctypes.c_void_p:
