@@ -57,6 +57,8 @@ def parse_args():
     ap.add_argument("--variant", choices=["fused", "split"], default="fused")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--pmc-probe", action="store_true")
+    ap.add_argument("--producer-steps", type=int, default=10,
+                    help="timed M=256 lm_head producer + gather calls (0: skip)")
     return ap.parse_args()
 
 
@@ -184,6 +186,57 @@ def main() -> int:
     gbps_cold = big_bytes / (us_cold * 1e-6) / 1e9
     gbps_hot = big_bytes / (us_hot * 1e-6) / 1e9
 
+    # ---------------- fused workload: lm_head producer + gather -------------
+    producer = None
+    if args.producer_steps > 0:
+        log("producer: generating the M=256 x 7168 hidden states and the 163840 x 7168 head weight")
+        x_bits = syn.hidden_states(wl)
+        xd = syn.to_torch_bf16(x_bits, dev)
+        w_dev = torch.empty((wl.tp, wl.shard, wl.hidden), dtype=torch.bfloat16, device=dev)
+        w_r0 = None
+        for r in range(wl.tp):
+            wr = syn.head_weight_shard(wl, r)
+            if r == 0:
+                w_r0 = wr
+            w_dev[r].copy_(syn.to_torch_bf16(wr, dev))
+        prod_out = torch.empty((wl.rows, wl.vocab), dtype=torch.bfloat16, device=dev)
+        prod_shards = torch.empty((wl.tp, wl.rows, wl.shard), dtype=torch.bfloat16, device=dev)
+        xptr = ctypes.c_void_p(xd.data_ptr())
+        wptrs = _lib.pointer_array([w_dev[r].data_ptr() for r in range(wl.tp)])
+        sptrs = _lib.pointer_array([prod_shards[r].data_ptr() for r in range(wl.tp)])
+        optr = ctypes.c_void_p(prod_out.data_ptr())
+        gg, lm = lib.hg_gemm_gather, lib.hg_lmhead
+        h = hg_big.handle
+        for _ in range(2):
+            rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
+            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, sh)
+        log(f"producer timed {args.producer_steps} x (GEMM + gather) and {args.producer_steps} x GEMM")
+        with Timer(torch, stream) as t_pg:
+            for _ in range(args.producer_steps):
+                rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
+        with Timer(torch, stream) as t_lm:
+            for _ in range(args.producer_steps):
+                rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, sh)
+        if rcs:
+            raise _lib.HgError(-abs(rcs), "timed producer loop")
+        flops = 2.0 * wl.rows * wl.hidden * wl.vocab
+        w_bytes = wl.vocab * wl.hidden * 2
+        us_pg = t_pg.ms * 1000.0 / args.producer_steps
+        us_lm = t_lm.ms * 1000.0 / args.producer_steps
+        producer = {"workload": "lm_head X[256,7168] @ W[163840,7168]^T (8 ranks x 20480) BF16, "
+                                "fp32 accumulate, epilogue pushes into the mailbox, then collect",
+                    "us_gemm_plus_gather": round(us_pg, 2),
+                    "us_gemm_alone": round(us_lm, 2),
+                    "gemm_tflops": round(flops / (us_lm * 1e-6) / 1e12, 1),
+                    "gemm_frac_of_mfma_bf16_peak": round(flops / (us_lm * 1e-6) / 2.5e15, 4),
+                    "gemm_weight_gbps": round(w_bytes / (us_lm * 1e-6) / 1e9, 1),
+                    "gemm_weight_frac_of_hbm_peak": round(w_bytes / (us_lm * 1e-6) / 8e12, 4)}
+        # the gather of the producer path against the oracle applied to the product's own shards
+        rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, sh)
+        rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
+        torch.cuda.synchronize()
+        del w_dev
+
     # ---------------- mailbox state after the runs --------------------------
     armed = torch.full((wd.cap, wd.vocab // 2), -(1 << 31), dtype=torch.int32, device=dev)
     armed_big = torch.full((wl.cap, wl.vocab // 2), -(1 << 31), dtype=torch.int32, device=dev)
@@ -236,6 +289,27 @@ def main() -> int:
         if not np.array_equal(syn.from_torch_bf16(big_out[0]), want_big):
             log("FAIL: M=256 output differs from the oracle")
             return 1
+        if producer is not None:
+            from oracle import gemm as ogemm
+
+            shards_bits = syn.from_torch_bf16(prod_shards)
+            if not np.array_equal(syn.from_torch_bf16(prod_out), og.gather_definition(list(shards_bits))):
+                log("FAIL: producer gather differs from the oracle on the product's shards")
+                return 1
+            # the GEMM oracle (float64) on a bounded sample: rank 0's first 1024 vocab rows
+            t0 = time.perf_counter()
+            ref = ogemm.lm_head_shard(x_bits, w_r0[:1024])
+            t_ref = time.perf_counter() - t0
+            err = ogemm.relative_frobenius_error(shards_bits[0][:, :1024], ref)
+            if err > 1e-2:
+                log(f"FAIL: GEMM relative error {err:.3e} on the sample")
+                return 1
+            sample_flops = 2.0 * wl.rows * wl.hidden * 1024
+            cpu["gemm_oracle"] = {"gflops": round(sample_flops / t_ref / 1e9, 2),
+                                  "sample": "oracle.gemm.lm_head_shard (numpy float64) on "
+                                            "X[256,7168] x rank 0's first 1024 weight rows",
+                                  "threads": "numpy/BLAS default",
+                                  "rel_frobenius_error_gpu_vs_oracle": err}
 
     # ---------------- counters (only if taken on this kernel source) --------
     traffic = None
@@ -277,6 +351,7 @@ def main() -> int:
         "roofline_m1": {"bound": "latency", "achieved": round(dec_bytes / (us_m1 * 1e-6) / 1e9, 1),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(dec_bytes / (us_m1 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "producer": producer,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_source_hash(),
     }

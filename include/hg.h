@@ -143,6 +143,37 @@ int hg_collect(hg_ctx *h, int m, void *out, void *stream);
  */
 int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *out, void *stream);
 
+/*
+ * The lm_head shard product that feeds the gather (API page, module
+ * description: the vocab-parallel lm_head produces the [M, V/TP] shards the
+ * gather collects; install_logits_gather takes the shard width from the head
+ * weight's first dimension): for every rank r,
+ *     shards_out[r] = X @ W_r^T,   BF16 inputs, fp32 accumulation, BF16
+ *                                  result rounded to nearest even.
+ * x:          device [m][hidden] BF16, row-major.
+ * w:          host array of tp device pointers; w[r] = rank r's head-weight
+ *             rows [shard][hidden] BF16, row-major.
+ * shards_out: host array of tp device pointers; shards_out[r] = [m][shard]
+ *             BF16, row-major; must not overlap x or w.
+ * HG_EINVAL unless 1 <= tp <= HG_MAX_TP, shard >= 32 and shard % 32 == 0,
+ * hidden >= 8 and hidden % 8 == 0, m >= 0, pointers non-NULL and 16-byte
+ * aligned. m == 0 does nothing. The result is deterministic (no split-K).
+ */
+int hg_lmhead(int tp, int shard, const void *x, const void *const *w, int hidden, int m,
+              void *const *shards_out, void *stream);
+
+/*
+ * Producer and gather: the lm_head product above whose epilogue pushes its
+ * words -- sentinel rewritten -- straight into rows 0..m-1 of the current
+ * parity (no shard round trip), then the collect kernel polls, copies to
+ * `out` ([m][tp*shard] BF16) and re-arms; the parity flips. Two launches on
+ * `stream`. When shards_out is non-NULL the product's BF16 shards are also
+ * written there, bytes as computed. Declines, state errors and pointer rules
+ * as hg_gather; the size rules of hg_lmhead also apply (HG_EINVAL).
+ */
+int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hidden, int m, void *out,
+                   void *const *shards_out, void *stream);
+
 /* The parity the next served call will use (0 or 1), or HG_EINVAL. */
 int hg_parity(const hg_ctx *h);
 

@@ -50,6 +50,8 @@ SIGNATURES = {
     "hg_push_ranks": (_i, [_ctxp, ctypes.POINTER(_vp), _i, _ull, _vp]),
     "hg_collect": (_i, [_ctxp, _i, _vp, _vp]),
     "hg_stock_gather": (_i, [_i, _i, ctypes.POINTER(_vp), _i, _vp, _vp]),
+    "hg_lmhead": (_i, [_i, _i, _vp, ctypes.POINTER(_vp), _i, _i, ctypes.POINTER(_vp), _vp]),
+    "hg_gemm_gather": (_i, [_ctxp, _vp, ctypes.POINTER(_vp), _i, _i, _vp, ctypes.POINTER(_vp), _vp]),
     "hg_parity": (_i, [_ctxp]),
     "hg_mailbox": (_i, [_ctxp, _i, ctypes.POINTER(_vp), ctypes.POINTER(_size)]),
     "hg_copy_mailbox": (_i, [_ctxp, _i, _vp, _vp]),

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhg.so")
-SOURCES = ["hg_api.cpp", "hg_kernels.hip"]
+SOURCES = ["hg_api.cpp", "hg_kernels.hip", "hg_lmhead.hip"]
 ARCH = "gfx950"
 
 

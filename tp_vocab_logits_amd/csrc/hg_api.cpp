@@ -396,6 +396,81 @@ HG_API int hg_stock_gather(int tp, int shard, const void *const *shards, int m, 
   return HG_OK;
 }
 
+namespace {
+
+// Size and pointer rules of the lm_head product; fills the kernel tables.
+int check_lmhead(int tp, int shard, const void *x, const void *const *w, int hidden, int m,
+                 void *const *shards_out, ShardTable *wt, hg::OutTable *ot) {
+  if (tp < 1 || tp > HG_MAX_TP || shard < 32 || shard % 32 != 0 || hidden < 8 || hidden % 8 != 0 ||
+      m < 0)
+    return HG_EINVAL;
+  if (static_cast<long long>(tp) * shard >= (1ll << 31)) return HG_EINVAL;
+  if (m == 0) return HG_OK;  // nothing is read or written
+  if (!x || !aligned16(x) || !w) return HG_EINVAL;
+  memset(wt, 0, sizeof *wt);
+  memset(ot, 0, sizeof *ot);
+  const size_t x_bytes = static_cast<size_t>(m) * hidden * 2;
+  const size_t w_bytes = static_cast<size_t>(shard) * hidden * 2;
+  const size_t o_bytes = static_cast<size_t>(m) * shard * 2;
+  for (int r = 0; r < tp; ++r) {
+    if (!w[r] || !aligned16(w[r])) return HG_EINVAL;
+    wt->p[r] = static_cast<const u32x4 *>(w[r]);
+    if (shards_out) {
+      void *o = shards_out[r];
+      if (!o || !aligned16(o)) return HG_EINVAL;
+      if (overlaps(o, o_bytes, x, x_bytes) || overlaps(o, o_bytes, w[r], w_bytes)) return HG_EINVAL;
+      ot->p[r] = static_cast<uint32_t *>(o);
+    }
+  }
+  return HG_OK;
+}
+
+}  // namespace
+
+HG_API int hg_lmhead(int tp, int shard, const void *x, const void *const *w, int hidden, int m,
+                     void *const *shards_out, void *stream) {
+  if (!shards_out) return HG_EINVAL;
+  ShardTable wt;
+  hg::OutTable ot;
+  const int rc = check_lmhead(tp, shard, x, w, hidden, m, shards_out, &wt, &ot);
+  if (rc != HG_OK) return rc;
+  if (m == 0) return HG_OK;
+  HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, true, nullptr, m, hidden, shard,
+                            tp, static_cast<hipStream_t>(stream)));
+  return HG_OK;
+}
+
+HG_API int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hidden, int m,
+                          void *out, void *const *shards_out, void *stream) {
+  if (!h || m < 0) return HG_EINVAL;
+  if (h->pending_m >= 0) return HG_ESTATE;
+  if (m == 0 || m > h->cap) return HG_EDECLINE;
+  const int cs = capture_state(static_cast<hipStream_t>(stream));
+  if (cs != HG_OK) return cs;
+  int rc = check_device(h);
+  if (rc != HG_OK) return rc;
+  ShardTable wt;
+  hg::OutTable ot;
+  rc = check_lmhead(h->tp, h->shard, x, w, hidden, m, shards_out, &wt, &ot);
+  if (rc != HG_OK) return rc;
+  const size_t out_bytes = static_cast<size_t>(m) * h->row_bytes();
+  const size_t box_bytes = static_cast<size_t>(2) * h->cap * h->row_bytes();
+  if (!out || !aligned16(out) || overlaps(out, out_bytes, h->box, box_bytes) ||
+      overlaps(out, out_bytes, x, static_cast<size_t>(m) * hidden * 2))
+    return HG_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  u32x4 *box = h->parity_box(h->parity);
+  HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, shards_out != nullptr,
+                            reinterpret_cast<uint32_t *>(box), m, hidden, h->shard, h->tp, s));
+  const hg::Modes md = pick_modes(h, h->tune.split_vpt, m);
+  const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
+  const int block = h->tune.split_block;
+  HIP_TRY(hg::launch_collect(g, md, box, used_box_bytes(h, m), static_cast<u32x4 *>(out),
+                             h->status, h->poll_limit, split_grid(h, g, block), block, s));
+  h->parity ^= 1;
+  return HG_OK;
+}
+
 HG_API int hg_parity(const hg_ctx *h) { return h ? h->parity : HG_EINVAL; }
 
 HG_API int hg_mailbox(const hg_ctx *h, int parity, const void **dev, size_t *bytes) {

@@ -26,6 +26,13 @@ struct ShardTableN {
 using ShardTable = ShardTableN<HG_MAX_TP>;
 constexpr int kSmallTable = 8;
 
+// Per-rank output blocks as 32-bit words (the lm_head kernel's shard copies).
+template <int N>
+struct OutTableN {
+  uint32_t *p[N];
+};
+using OutTable = OutTableN<HG_MAX_TP>;
+
 // Work geometry of one launch. Work is cut into wave-sized chunks: a chunk is
 // 64 * vpt consecutive vectors of one (row, rank) segment, so the rank -- and
 // with it the shard pointer -- is the same for every lane of a wave.
@@ -79,6 +86,14 @@ hipError_t launch_collect(const Geometry &g, const Modes &md, u32x4 *box, unsign
                           int block, hipStream_t s);
 hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *out, int grid,
                         int block, hipStream_t s);
+
+// The lm_head shard product X [m][hidden] @ W_r^T (W_r = w.p[r], [shard][hidden]),
+// BF16 in, fp32 accumulate, BF16 out. `box` (mailbox rows of the current
+// parity, [m][tp*shard] words) receives the words with the sentinel
+// rewritten, when non-null; `shards_out` receives the plain BF16 shards when
+// `keep`. Needs shard % 32 == 0 and hidden % 8 == 0.
+hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &shards_out, bool keep,
+                         uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s);
 
 // Resident workgroups per CU of the fused kernel variant at a block size.
 hipError_t fused_blocks_per_cu(const Modes &md, int tp, int block, int *blocks);

@@ -22,7 +22,7 @@ import torch
 from . import _lib
 from ._lib import HG_EDECLINE, HG_OK, HgError, check, lib, pointer_array
 
-__all__ = ["HeadGather", "HgError", "stock_gather"]
+__all__ = ["HeadGather", "HgError", "lmhead", "stock_gather"]
 
 
 def _stream_handle(device: torch.device) -> ctypes.c_void_p:
@@ -72,6 +72,44 @@ def stock_gather(shards: torch.Tensor | Sequence[torch.Tensor], tp: int,
         check(lib().hg_stock_gather(tp, s, pointer_array(ptrs), m, ctypes.c_void_p(out.data_ptr()),
                                     _stream_handle(device)), "hg_stock_gather")
     return out
+
+
+def _weight_pointers(w, tp: int, shard: int, hidden: int) -> list[int]:
+    """Pointers of the TP head-weight blocks: a ``[TP*S, H]`` (or ``[TP, S, H]``)
+    tensor, or a sequence of TP ``[S, H]`` tensors."""
+    if isinstance(w, torch.Tensor):
+        if w.dtype != torch.bfloat16 or not w.is_contiguous() or w.numel() != tp * shard * hidden:
+            raise ValueError(f"head weight must be a contiguous BF16 [{tp * shard}, {hidden}] tensor")
+        step = shard * hidden * w.element_size()
+        return [w.data_ptr() + r * step for r in range(tp)]
+    w = list(w)
+    if len(w) != tp:
+        raise ValueError(f"expected {tp} weight blocks, got {len(w)}")
+    for t in w:
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (shard, hidden) or not t.is_contiguous():
+            raise ValueError(f"every weight block must be a contiguous BF16 [{shard}, {hidden}] tensor")
+    return [t.data_ptr() for t in w]
+
+
+def lmhead(x: torch.Tensor, w, tp: int, shard: int,
+           shards_out: torch.Tensor | None = None) -> torch.Tensor:
+    """The lm_head shard product ``[TP, M, S] = X @ W_r^T`` per rank (BF16 in,
+    fp32 accumulate, BF16 out), in the library's MFMA kernel."""
+    if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+        raise ValueError("x must be a contiguous BF16 [M, H] tensor")
+    m, hidden = (int(v) for v in x.shape)
+    wp = _weight_pointers(w, tp, shard, hidden)
+    if shards_out is None:
+        shards_out = torch.empty((tp, m, shard), dtype=torch.bfloat16, device=x.device)
+    elif (shards_out.dtype != torch.bfloat16 or tuple(shards_out.shape) != (tp, m, shard)
+          or not shards_out.is_contiguous()):
+        raise ValueError(f"shards_out must be a contiguous BF16 [{tp}, {m}, {shard}] tensor")
+    step = m * shard * 2
+    op = [shards_out.data_ptr() + r * step for r in range(tp)]
+    with torch.cuda.device(x.device):
+        check(lib().hg_lmhead(tp, shard, ctypes.c_void_p(x.data_ptr()), pointer_array(wp), hidden, m,
+                              pointer_array(op), _stream_handle(x.device)), "hg_lmhead")
+    return shards_out
 
 
 class HeadGather:
@@ -166,6 +204,34 @@ class HeadGather:
         if rc == HG_EDECLINE:
             raise HgError(_lib.HG_ESTATE, "hg_collect declined (stream capturing)")
         check(rc, "hg_collect")
+        return out
+
+    def gemm_gather(self, x: torch.Tensor, w, out: torch.Tensor | None = None,
+                    shards_out: torch.Tensor | None = None) -> torch.Tensor:
+        """Producer + gather: the lm_head product ``X @ W_r^T`` with its
+        epilogue pushing into the mailbox, then poll/copy/re-arm. ``w`` is the
+        ``[TP*S, H]`` head weight (or TP ``[S, H]`` blocks). When given,
+        ``shards_out`` ``[TP, M, S]`` also receives the product's BF16 shards.
+        Raises on a declined call (no stock producer exists here)."""
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
+            raise ValueError("x must be a contiguous BF16 [M, H] tensor")
+        m, hidden = (int(v) for v in x.shape)
+        wp = _weight_pointers(w, self.tp, self.shard, hidden)
+        out = self._out(m, out)
+        op = None
+        if shards_out is not None:
+            if (shards_out.dtype != torch.bfloat16 or tuple(shards_out.shape) != (self.tp, m, self.shard)
+                    or not shards_out.is_contiguous()):
+                raise ValueError("shards_out must be a contiguous BF16 [TP, M, S] tensor")
+            step = m * self.shard * 2
+            op = pointer_array([shards_out.data_ptr() + r * step for r in range(self.tp)])
+        with torch.cuda.device(self.device):
+            rc = lib().hg_gemm_gather(self._h, ctypes.c_void_p(x.data_ptr()), pointer_array(wp), hidden,
+                                      m, ctypes.c_void_p(out.data_ptr()), op,
+                                      _stream_handle(self.device))
+        if rc == HG_EDECLINE:
+            raise HgError(_lib.HG_EINVAL, "hg_gemm_gather declined (rows outside 1..cap or capturing)")
+        check(rc, "hg_gemm_gather")
         return out
 
     def arm(self) -> None:
