@@ -209,14 +209,14 @@ def main() -> int:
         h = hg_big.handle
         for _ in range(2):
             rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
-            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, sh)
+            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
         log(f"producer timed {args.producer_steps} x (GEMM + gather) and {args.producer_steps} x GEMM")
         with Timer(torch, stream) as t_pg:
             for _ in range(args.producer_steps):
                 rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
         with Timer(torch, stream) as t_lm:
             for _ in range(args.producer_steps):
-                rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, sh)
+                rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
         if rcs:
             raise _lib.HgError(-abs(rcs), "timed producer loop")
         flops = 2.0 * wl.rows * wl.hidden * wl.vocab
@@ -232,7 +232,7 @@ def main() -> int:
                     "gemm_weight_gbps": round(w_bytes / (us_lm * 1e-6) / 1e9, 1),
                     "gemm_weight_frac_of_hbm_peak": round(w_bytes / (us_lm * 1e-6) / 8e12, 4)}
         # the gather of the producer path against the oracle applied to the product's own shards
-        rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, sh)
+        rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
         rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
         torch.cuda.synchronize()
         del w_dev

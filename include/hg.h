@@ -158,9 +158,17 @@ int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *o
  * HG_EINVAL unless 1 <= tp <= HG_MAX_TP, shard >= 32 and shard % 32 == 0,
  * hidden >= 8 and hidden % 8 == 0, m >= 0, pointers non-NULL and 16-byte
  * aligned. m == 0 does nothing. The result is deterministic (no split-K).
+ * variant: the implementation -- 0 the default (6); 1 256 output columns per
+ * workgroup with direct global-to-LDS loads, 32-wide K steps, 4 stages; 2
+ * 256 columns with loads staged through registers; 3 128 columns staged
+ * through registers; 4 as 1 with non-temporal weight loads; 5 as 1 with
+ * 64-wide K steps and 2 stages; 6 as 5 with non-temporal weight loads; 7
+ * 64-wide K steps with 2 X stages and 3 weight stages (all 160 KB of LDS).
+ * Every variant performs the same sequence of fp32 MFMA accumulations and
+ * gives the same bits.
  */
 int hg_lmhead(int tp, int shard, const void *x, const void *const *w, int hidden, int m,
-              void *const *shards_out, void *stream);
+              void *const *shards_out, int variant, void *stream);
 
 /*
  * Producer and gather: the lm_head product above whose epilogue pushes its
@@ -215,6 +223,8 @@ int hg_poll_status(hg_ctx *h, void *stream);
                                  1 128-bit loads, agent-coherent (sc1) policy;
                                  2 as 1 with the non-temporal hint                      */
 #define HG_TUNE_REARM_MODE 9  /* re-arm stores: 0 plain, 1 non-temporal                 */
+#define HG_TUNE_GEMM_VARIANT 10 /* hg_gemm_gather: lm_head implementation as for
+                                   hg_lmhead's `variant` (0: default)                 */
 int hg_set_tuning(hg_ctx *h, int knob, int value);
 int hg_get_tuning(const hg_ctx *h, int knob, int *value);
 

@@ -82,14 +82,18 @@ def test_hand_worked_golden_product():
     assert np.all(out[0, :, 4:] == 0)
 
 
+VARIANTS = [1, 2, 3, 4, 5, 6, 7]
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("tp,shard,hidden,m", [
     (1, 32, 8, 1), (2, 64, 72, 3), (3, 288, 136, 17), (8, 96, 512, 256), (2, 512, 1032, 300),
-    (5, 160, 64, 255), (64, 32, 64, 2)])
-def test_ragged_sizes_against_oracle(tp, shard, hidden, m):
-    note(f"lmhead ragged tp={tp} shard={shard} hidden={hidden} m={m}")
+    (5, 160, 64, 255), (64, 32, 64, 2), (2, 256, 40, 7)])
+def test_ragged_sizes_against_oracle(tp, shard, hidden, m, variant):
+    note(f"lmhead ragged tp={tp} shard={shard} hidden={hidden} m={m} variant={variant}")
     x = rand_bits((m, hidden), 0.5, 10 + m)
     w = rand_bits((tp, shard, hidden), 0.5, 20 + hidden)
-    out = bits(lmhead(dev(x), dev(w), tp, shard))
+    out = bits(lmhead(dev(x), dev(w), tp, shard, variant=variant))
     for r in range(tp):
         assert_close_to_oracle(out[r], x, w[r])
 
@@ -132,9 +136,11 @@ def test_full_size_producer_gather_m256():
     # the product itself, rank by rank, against the float64 oracle
     for r in range(tp):
         assert_close_to_oracle(sb[r], x, w_host[r])
-    # deterministic: the standalone product and a second producer call agree bit for bit
-    again = lmhead(xd, wd, tp, shard)
-    assert torch.equal(again.view(torch.int16), shards.view(torch.int16))
+    # deterministic: every implementation of the standalone product and a second
+    # producer call agree bit for bit
+    for variant in VARIANTS:
+        again = lmhead(xd, wd, tp, shard, variant=variant)
+        assert torch.equal(again.view(torch.int16), shards.view(torch.int16)), variant
     out2 = hg.gemm_gather(xd, wd)
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert hg.parity == 0 and hg.poll_status() == _lib.HG_OK

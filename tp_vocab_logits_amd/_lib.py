@@ -33,6 +33,7 @@ TUNE_POLL_SKEW = 6
 TUNE_PUSH_MODE = 7
 TUNE_POLL_MODE = 8
 TUNE_REARM_MODE = 9
+TUNE_GEMM_VARIANT = 10
 
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
@@ -50,7 +51,7 @@ SIGNATURES = {
     "hg_push_ranks": (_i, [_ctxp, ctypes.POINTER(_vp), _i, _ull, _vp]),
     "hg_collect": (_i, [_ctxp, _i, _vp, _vp]),
     "hg_stock_gather": (_i, [_i, _i, ctypes.POINTER(_vp), _i, _vp, _vp]),
-    "hg_lmhead": (_i, [_i, _i, _vp, ctypes.POINTER(_vp), _i, _i, ctypes.POINTER(_vp), _vp]),
+    "hg_lmhead": (_i, [_i, _i, _vp, ctypes.POINTER(_vp), _i, _i, ctypes.POINTER(_vp), _i, _vp]),
     "hg_gemm_gather": (_i, [_ctxp, _vp, ctypes.POINTER(_vp), _i, _i, _vp, ctypes.POINTER(_vp), _vp]),
     "hg_parity": (_i, [_ctxp]),
     "hg_mailbox": (_i, [_ctxp, _i, ctypes.POINTER(_vp), ctypes.POINTER(_size)]),

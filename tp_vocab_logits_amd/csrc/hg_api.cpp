@@ -60,9 +60,15 @@ struct Tuning {
   int push_mode = hg::kPushB128Sc1;
   int poll_mode = hg::kPollB128Sc1Nt;
   int rearm_mode = 1;
+  int gemm_variant = 0;  // lm_head implementation (hg::GemmVariant), 0: the default
 };
 
 constexpr int kGridPerCu = 4;
+constexpr int kDefaultGemmVariant = hg::kGemmDirectLds64Nt;
+
+bool valid_gemm_variant(int v) {
+  return v >= 0 && v <= hg::kGemmDirectLdsDeepW;
+}
 
 bool valid_block(int b) { return b == 64 || b == 128 || b == 256 || b == 512 || b == 1024; }
 bool valid_vpt(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8; }
@@ -428,15 +434,16 @@ int check_lmhead(int tp, int shard, const void *x, const void *const *w, int hid
 }  // namespace
 
 HG_API int hg_lmhead(int tp, int shard, const void *x, const void *const *w, int hidden, int m,
-                     void *const *shards_out, void *stream) {
-  if (!shards_out) return HG_EINVAL;
+                     void *const *shards_out, int variant, void *stream) {
+  if (!shards_out || !valid_gemm_variant(variant)) return HG_EINVAL;
   ShardTable wt;
   hg::OutTable ot;
   const int rc = check_lmhead(tp, shard, x, w, hidden, m, shards_out, &wt, &ot);
   if (rc != HG_OK) return rc;
   if (m == 0) return HG_OK;
   HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, true, nullptr, m, hidden, shard,
-                            tp, static_cast<hipStream_t>(stream)));
+                            tp, variant ? variant : kDefaultGemmVariant,
+                            static_cast<hipStream_t>(stream)));
   return HG_OK;
 }
 
@@ -461,7 +468,8 @@ HG_API int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hi
   hipStream_t s = static_cast<hipStream_t>(stream);
   u32x4 *box = h->parity_box(h->parity);
   HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, shards_out != nullptr,
-                            reinterpret_cast<uint32_t *>(box), m, hidden, h->shard, h->tp, s));
+                            reinterpret_cast<uint32_t *>(box), m, hidden, h->shard, h->tp,
+                            h->tune.gemm_variant ? h->tune.gemm_variant : kDefaultGemmVariant, s));
   const hg::Modes md = pick_modes(h, h->tune.split_vpt, m);
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
   const int block = h->tune.split_block;
@@ -554,6 +562,10 @@ HG_API int hg_set_tuning(hg_ctx *h, int knob, int value) {
       if (value != 0 && value != 1) return HG_EINVAL;
       h->tune.rearm_mode = value;
       return HG_OK;
+    case HG_TUNE_GEMM_VARIANT:
+      if (!valid_gemm_variant(value)) return HG_EINVAL;
+      h->tune.gemm_variant = value;
+      return HG_OK;
     default:
       return HG_EINVAL;
   }
@@ -571,6 +583,7 @@ HG_API int hg_get_tuning(const hg_ctx *h, int knob, int *value) {
     case HG_TUNE_PUSH_MODE: *value = h->tune.push_mode; return HG_OK;
     case HG_TUNE_POLL_MODE: *value = h->tune.poll_mode; return HG_OK;
     case HG_TUNE_REARM_MODE: *value = h->tune.rearm_mode; return HG_OK;
+    case HG_TUNE_GEMM_VARIANT: *value = h->tune.gemm_variant; return HG_OK;
     default: return HG_EINVAL;
   }
 }

@@ -91,9 +91,20 @@ hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, u32x4 
 // BF16 in, fp32 accumulate, BF16 out. `box` (mailbox rows of the current
 // parity, [m][tp*shard] words) receives the words with the sentinel
 // rewritten, when non-null; `shards_out` receives the plain BF16 shards when
-// `keep`. Needs shard % 32 == 0 and hidden % 8 == 0.
+// `keep`. Needs shard % 32 == 0 and hidden % 8 == 0. `variant` picks the
+// implementation (all give the same bits).
+enum GemmVariant : int {
+  kGemmDirectLds = 1,  // 256 columns per workgroup, global -> LDS loads, 4 stages
+  kGemmStaged256 = 2,  // 256 columns per workgroup, loads staged through registers
+  kGemmStaged128 = 3,  // 128 columns per workgroup, loads staged through registers
+  kGemmDirectLdsNt = 4,    // as 1, weight loads non-temporal
+  kGemmDirectLds64 = 5,    // as 1 with 64-wide K steps, 2 stages
+  kGemmDirectLds64Nt = 6,  // as 5, weight loads non-temporal
+  kGemmDirectLdsDeepW = 7,  // 64-wide K steps, 2 X stages + 3 weight stages, weights nt
+};
 hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &shards_out, bool keep,
-                         uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s);
+                         uint32_t *box, int m, int hidden, int shard, int tp, int variant,
+                         hipStream_t s);
 
 // Resident workgroups per CU of the fused kernel variant at a block size.
 hipError_t fused_blocks_per_cu(const Modes &md, int tp, int block, int *blocks);

@@ -11,19 +11,20 @@
 // custom all-gather for TP logits" (Test Result) has the gather overlap the
 // tail of this GEMM; here the GEMM's epilogue performs the push itself.
 //
-// Work decomposition: a workgroup of 8 waves owns a 256-row x 256-column
-// output tile (all of M = 256 at once, 256 consecutive vocab columns); wave w
-// computes rows 128*(w%2) .. +128 and columns 64*(w/2) .. +64 as 4 x 2 blocks
-// of v_mfma_f32_32x32x16_bf16. Per 64-wide K step the X tile [256 x 64] is
-// staged in LDS (double-buffered, rows padded by 16 bytes against bank
-// conflicts) and shared by the 8 waves; each wave streams its own 64 weight
-// rows straight from HBM into registers, 64 contiguous bytes per lane, one
-// step ahead of the matrix cores.
+// Work decomposition: a workgroup of 2*NCP waves owns a 256-row x 64*NCP
+// column output tile (all of M = 256 at once); wave w computes rows
+// 128*(w%2) .. +128 and columns 64*(w/2) .. +64 as 4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16. Per 64-wide K step both operand tiles -- X
+// [256 x 64] and the weight rows [64*NCP x 64] -- are staged in LDS (two
+// stages, rows padded by 16 bytes against bank conflicts). Global loads are
+// fully coalesced (eight lanes cover one 128-byte row segment) and run one K
+// step ahead of the matrix cores through registers.
 //
-// K order inside a step: lane l supplies 8 consecutive K elements per MFMA,
-// and lanes 0-31 / 32-63 cover K offsets 0-31 / 32-63 of the step across the
-// four MFMAs (sub-step j takes offsets 8j..8j+7 of each half). A and B use the
-// same assignment, so every product X[m,k] * W[n,k] is summed exactly once.
+// K order: lane l supplies 8 consecutive K elements per MFMA. Per 32-wide
+// slice of K, the first MFMA takes offsets 0-7 (lanes 0-31) and 16-23 (lanes
+// 32-63), the second 8-15 and 24-31; slices follow in order. A and B use the
+// same assignment, so every product X[m,k] * W[n,k] is summed exactly once,
+// and every variant below performs the same sequence of MFMAs (same bits).
 
 #include "hg_internal.h"
 
@@ -36,11 +37,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 constexpr int kTM = 256;
-constexpr int kTN = 256;
 constexpr int kTK = 64;
-constexpr int kThreads = 512;
 constexpr int kLdsRow = kTK + 8;  // BF16 per LDS row: 64 + 16-byte pad
-constexpr int kLdsBuf = kTM * kLdsRow;
 
 __device__ __forceinline__ u32x4 load_stream(const u32x4 *p) {
   return __builtin_nontemporal_load(p);
@@ -56,64 +54,82 @@ __device__ __forceinline__ uint32_t swap_adjacent(uint32_t v) {
       __builtin_amdgcn_mov_dpp(static_cast<int>(v), 0xB1 /* quad_perm 1,0,3,2 */, 0xF, 0xF, true));
 }
 
-template <int NT, bool PUSH, bool KEEP>
-__global__ __launch_bounds__(kThreads) void k_lmhead(const u32x4 *x, ShardTableN<NT> w,
-                                                     OutTableN<NT> shards_out, uint32_t *box,
-                                                     int m, int hidden, int shard, int vocab) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2][kLdsBuf];
+template <int NT, int NCP, bool PUSH, bool KEEP>
+__global__ __launch_bounds__(NCP * 128) void k_lmhead(const u32x4 *x, ShardTableN<NT> w,
+                                                      OutTableN<NT> shards_out, uint32_t *box,
+                                                      int m, int hidden, int shard, int vocab) {
+  constexpr int kThreads = NCP * 128;
+  constexpr int kTN = 64 * NCP;
+  constexpr int kStage = (kTM + kTN) * kLdsRow;      // BF16 per LDS stage
+  constexpr int kXLoads = kTM * 8 / kThreads;        // 16-byte loads per thread per step
+  constexpr int kWLoads = kTN * 8 / kThreads;
+  constexpr int kLoads = kXLoads + kWLoads;
+  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * kStage];
 
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int mh = wave & 1;   // row half of the tile
-  const int nq = wave >> 1;  // column quarter of the tile
+  const int nq = wave >> 1;  // 64-column group of the tile
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int n0 = static_cast<int>(blockIdx.x) * kTN;
   const int m0 = static_cast<int>(blockIdx.y) * kTM;
   const int hv = hidden >> 3;  // 16-byte vectors per X / W row
   const int steps = (hidden + kTK - 1) / kTK;
+  const int seg = tid & 7;     // 16-byte segment of a 128-byte row step
 
-  // X staging: thread -> (tile row, 32-element half of the K step).
-  const int xr = tid >> 1, xh = tid & 1;
-  const bool x_ok = m0 + xr < m;
-  const u32x4 *xp = x + static_cast<long long>(x_ok ? m0 + xr : 0) * hv + xh * 4;
-
-  // Weight rows of this lane's two 32-column blocks (uniform rank per block).
-  const u32x4 *wp[2];
-  bool col_ok[2];
+  // Staging loads: load q of thread t covers LDS row (q*kThreads + t)/8 of the
+  // stage, segment t%8. Rows 0..255 are X rows, the rest weight rows; the
+  // split falls between loads, and a wave's 8 weight rows lie in one rank
+  // (shard % 32 == 0), so the rank is uniform per wave and load.
+  int xoff[kXLoads];
+  bool xok[kXLoads];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int c0 = n0 + 64 * nq + 32 * cb;
-    col_ok[cb] = c0 < vocab;
-    const int r = col_ok[cb] ? c0 / shard : 0;
-    const int s = col_ok[cb] ? c0 - r * shard + l32 : 0;
-    wp[cb] = col_ok[cb] ? w.p[r] + static_cast<long long>(s) * hv + half * 4 : nullptr;
+  for (int q = 0; q < kXLoads; ++q) {
+    const int row = (q * kThreads + tid) >> 3;
+    xok[q] = m0 + row < m;
+    xoff[q] = (xok[q] ? (m0 + row) * hv : 0) + seg;
+  }
+  const u32x4 *wbase[kWLoads];
+  int woff[kWLoads];
+  bool wok[kWLoads];
+#pragma unroll
+  for (int q = 0; q < kWLoads; ++q) {
+    const int wrow = ((q * kThreads + tid) >> 3);  // 0 .. kTN-1
+    const int n = n0 + wrow;
+    const int n_wave = __builtin_amdgcn_readfirstlane(n0 + ((q * kThreads + wave * kWave) >> 3));
+    wok[q] = n < vocab;
+    const int r = n_wave < vocab ? n_wave / shard : 0;
+    wbase[q] = w.p[r];
+    woff[q] = (wok[q] ? (n - r * shard) * hv : 0) + seg;
   }
 
   const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 xs[4], wc[2][4], wn[2][4];
+  u32x4 P[kLoads];
 
-  auto load_x = [&](int kb) {
+  auto load_step = [&](int kb) {
+    const int kv = kb * 8;
+    const bool kok = kv + seg < hv;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bool ok = x_ok && kb * kTK + xh * 32 + 8 * j < hidden;
-      xs[j] = ok ? xp[kb * 8 + j] : zero;
+    for (int q = 0; q < kXLoads; ++q) {
+      const bool ok = kok && xok[q];
+      const u32x4 v = x[ok ? xoff[q] + kv : 0];
+      P[q] = ok ? v : zero;
+    }
+#pragma unroll
+    for (int q = 0; q < kWLoads; ++q) {
+      const bool ok = kok && wok[q];
+      const u32x4 v = load_stream(wbase[q] + (ok ? woff[q] + kv : 0));
+      P[kXLoads + q] = ok ? v : zero;
     }
   };
-  auto store_x = [&](int buf) {
+  auto store_step = [&](int stage) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<u32x4 *>(&lds[buf][xr * kLdsRow + xh * 32 + 8 * j]) = xs[j];
-  };
-  auto load_w = [&](int kb, u32x4 (&dst)[2][4]) {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool ok = col_ok[cb] && kb * kTK + half * 32 + 8 * j < hidden;
-        dst[cb][j] = ok ? load_stream(wp[cb] + kb * 8 + j) : zero;
-      }
+    for (int q = 0; q < kLoads; ++q) {
+      const int row = (q * kThreads + tid) >> 3;
+      *reinterpret_cast<u32x4 *>(&lds[stage * kStage + row * kLdsRow + seg * 8]) = P[q];
+    }
   };
 
   f32x16 acc[4][2];
@@ -122,38 +138,34 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(const u32x4 *x, ShardTableN
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[i][cb] = f32x16{};
 
-  load_x(0);
-  load_w(0, wc);
-  store_x(0);
+  // Pipeline: LDS stage kb%2 holds step kb while the registers carry step kb+1.
+  load_step(0);
+  store_step(0);
   __syncthreads();
-
   for (int kb = 0; kb < steps; ++kb) {
-    const int buf = kb & 1;
+    const int stage = kb & 1;
     const bool more = kb + 1 < steps;
-    if (more) {
-      load_x(kb + 1);
-      load_w(kb + 1, wn);
-    }
+    if (more) load_step(kb + 1);
+    const __bf16 *sa = &lds[stage * kStage];
+    const __bf16 *sb = &lds[stage * kStage + kTM * kLdsRow];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bf16x8 b0 = __builtin_bit_cast(bf16x8, wc[0][j]);
-      const bf16x8 b1 = __builtin_bit_cast(bf16x8, wc[1][j]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 128 * mh + 32 * i + l32;
-        const bf16x8 a =
-            *reinterpret_cast<const bf16x8 *>(&lds[buf][row * kLdsRow + 32 * half + 8 * j]);
-        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[i][0], 0, 0, 0);
-        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[i][1], 0, 0, 0);
-      }
-    }
-    if (more) {
-      store_x(buf ^ 1);
+      // The same K order as the direct-to-LDS variant (two 32-wide halves of
+      // the step in turn), so every variant issues the same MFMA sequence.
+      const int koff = 32 * (j >> 1) + 16 * half + 8 * (j & 1);
+      bf16x8 b[2];
 #pragma unroll
       for (int cb = 0; cb < 2; ++cb)
+        b[cb] = *reinterpret_cast<const bf16x8 *>(&sb[(64 * nq + 32 * cb + l32) * kLdsRow + koff]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) wc[cb][j] = wn[cb][j];
+      for (int i = 0; i < 4; ++i) {
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8 *>(&sa[(128 * mh + 32 * i + l32) * kLdsRow + koff]);
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[1], acc[i][1], 0, 0, 0);
+      }
     }
+    if (more) store_step(stage ^ 1);
     __syncthreads();
   }
 
@@ -167,8 +179,8 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(const u32x4 *x, ShardTableN
   const int words_per_row = vocab >> 1;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
-    if (!col_ok[cb]) continue;
     const int c0 = n0 + 64 * nq + 32 * cb;
+    if (c0 >= vocab) continue;
     const int r = c0 / shard;
     const int s_even = c0 - r * shard + (l32 & ~1);  // even column of this lane's word
     const int wcol = s_even >> 1;
@@ -203,7 +215,200 @@ __global__ __launch_bounds__(kThreads) void k_lmhead(const u32x4 *x, ShardTableN
   }
 }
 
-template <int NT>
+// Variant with direct global -> LDS loads (gfx950 global_load_lds_dwordx4):
+// no register staging, so more K steps can be in flight. K step KS (32 or 64
+// elements: 4 or 8 slots of 16 bytes per row), ST LDS stages of [256 X rows +
+// 256 weight rows], loads issued ST-1 steps ahead. A wave's load instruction
+// fills 1 KB of LDS contiguously, lane-major (1024/(2*KS) rows of 2*KS
+// bytes); the lane owning slot s of a row loads the row's K segment
+// s ^ swz(row), so the stored layout is XOR-swizzled and the fragment reads (8
+// or 16 consecutive rows, one K segment) hit distinct banks. WNT marks the
+// weight loads non-temporal (streamed once).
+template <int KS>
+__device__ __forceinline__ int dswz(int row) {
+  if constexpr (KS == 32)
+    return ((row >> 1) ^ (row >> 3)) & 3;
+  else
+    return (row ^ (row >> 3)) & 7;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  // s_waitcnt vmcnt(N) (N < 64) without waiting on LDS or export counters
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
+
+template <int NT, int KS, int ST, bool WNT, bool PUSH, bool KEEP>
+__global__ __launch_bounds__(512) void k_lmhead_dma(const u32x4 *x, ShardTableN<NT> w,
+                                                    OutTableN<NT> shards_out, uint32_t *box, int m,
+                                                    int hidden, int shard, int vocab) {
+  constexpr int kTN = 256;
+  constexpr int kRowBytes = KS * 2;
+  constexpr int kSlots = KS / 8;                   // 16-byte slots per row
+  constexpr int kRowsPerInst = 1024 / kRowBytes;   // rows one wave instruction fills
+  constexpr int kStageBytes = 512 * kRowBytes;
+  constexpr int kInst = 512 / (8 * kRowsPerInst);  // instructions per wave per step
+  constexpr int kXInst = kInst / 2;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[ST * kStageBytes];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int mh = wave & 1;
+  const int nq = wave >> 1;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int n0 = static_cast<int>(blockIdx.x) * kTN;
+  const int m0 = static_cast<int>(blockIdx.y) * kTM;
+  const int hv = hidden >> 3;
+  const int steps = (hidden + KS - 1) / KS;
+
+  // Instruction q of wave w fills stage rows kRowsPerInst*(8q+w) .. : the
+  // first kXInst instructions X rows, the rest weight rows.
+  const int lrow = lane / kSlots, lslot = lane % kSlots;
+  const u32x4 *src[kInst];
+  bool ok[kInst];
+  int seg[kInst];
+#pragma unroll
+  for (int q = 0; q < kInst; ++q) {
+    const int srow = kRowsPerInst * (8 * q + wave) + lrow;  // stage row
+    seg[q] = lslot ^ dswz<KS>(srow);
+    if (q < kXInst) {
+      const int row = srow;
+      ok[q] = m0 + row < m;
+      src[q] = x + static_cast<long long>(ok[q] ? m0 + row : 0) * hv;
+    } else {
+      const int row = srow - 256;
+      const int n = n0 + row;
+      const int n_wave = __builtin_amdgcn_readfirstlane(n0 + kRowsPerInst * (8 * q + wave) - 256);
+      ok[q] = n < vocab;
+      const int r = n_wave < vocab ? n_wave / shard : 0;
+      src[q] = w.p[r] + static_cast<long long>(ok[q] ? n - r * shard : 0) * hv;
+    }
+  }
+  // A lane whose row is out of range (or whose K segment is past `hidden`)
+  // loads from a valid address; its slot is cleared before use.
+  auto issue = [&](int kb) {
+    const int stage = kb % ST;
+#pragma unroll
+    for (int q = 0; q < kInst; ++q) {
+      const int kv = kb * kSlots + seg[q];
+      const u32x4 *p = src[q] + (ok[q] && kv < hv ? kv : 0);
+      __attribute__((address_space(3))) void *dst =
+          (__attribute__((address_space(3))) void *)(lds + stage * kStageBytes +
+                                                     kRowsPerInst * (8 * q + wave) * kRowBytes);
+      if (q >= kXInst && WNT)
+        __builtin_amdgcn_global_load_lds(p, dst, 16, 0, 2 /* nt */);
+      else
+        __builtin_amdgcn_global_load_lds(p, dst, 16, 0, 0);
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[i][cb] = f32x16{};
+
+  const bool tails = hidden % KS != 0 || m0 + kTM > m;
+  for (int p = 0; p < ST - 1 && p < steps; ++p) issue(p);
+  for (int kb = 0; kb < steps; ++kb) {
+    // Wait for this wave's loads of step kb; later steps stay in flight.
+    const int left = steps - 1 - kb;
+    if (ST >= 4 && left >= 2)
+      wait_vm<(ST >= 4 ? 2 : 0) * kInst>();
+    else if (ST >= 3 && left >= 1)
+      wait_vm<kInst>();
+    else
+      wait_vm<0>();
+    // Every wave's part of step kb is in LDS once all waves pass the
+    // barrier. A plain s_barrier: __syncthreads() would also wait for the
+    // later steps' loads still in flight.
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+    const int stage = kb % ST;
+    unsigned char *sbase = lds + stage * kStageBytes;
+    if (tails) {
+#pragma unroll
+      for (int q = 0; q < kInst; ++q) {
+        const int kv = kb * kSlots + seg[q];
+        if (!(ok[q] && kv < hv))
+          *reinterpret_cast<u32x4 *>(sbase + (kRowsPerInst * (8 * q + wave) + lrow) * kRowBytes +
+                                     lslot * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (ST > 1 && kb + ST - 1 < steps) issue(kb + ST - 1);
+#pragma unroll
+    for (int j = 0; j < KS / 16; ++j) {
+      // K segment of this lane for MFMA j: 32-wide slice j/2, half, j%2.
+      const int g = 4 * (j >> 1) + 2 * half + (j & 1);
+      bf16x8 b[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int row = 256 + 64 * nq + 32 * cb + l32;
+        b[cb] = *reinterpret_cast<const bf16x8 *>(sbase + row * kRowBytes +
+                                                   ((g ^ dswz<KS>(row)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 128 * mh + 32 * i + l32;
+        const bf16x8 a = *reinterpret_cast<const bf16x8 *>(sbase + row * kRowBytes +
+                                                            ((g ^ dswz<KS>(row)) << 4));
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[1], acc[i][1], 0, 0, 0);
+      }
+    }
+    if (ST == 1) {
+      // single stage: the next step may overwrite only after every wave read
+      __syncthreads();
+      if (kb + 1 < steps) issue(kb + 1);
+    }
+  }
+
+  const bool even = (l32 & 1) == 0;
+  const int words_per_shard_row = shard >> 1;
+  const int words_per_row = vocab >> 1;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int c0 = n0 + 64 * nq + 32 * cb;
+    if (c0 >= vocab) continue;
+    const int r = c0 / shard;
+    const int s_even = c0 - r * shard + (l32 & ~1);
+    const int wcol = s_even >> 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[t] = bf16_bits(acc[i][cb][4 * q + t]);
+        const uint32_t send = even ? (b[1] | (b[3] << 16)) : (b[0] | (b[2] << 16));
+        const uint32_t recv = swap_adjacent(send);
+        const uint32_t w0 = even ? (b[0] | (recv << 16)) : ((recv & 0xFFFFu) | (b[1] << 16));
+        const uint32_t w1 = even ? (b[2] | (recv & 0xFFFF0000u)) : ((recv >> 16) | (b[3] << 16));
+        const int rbase = m0 + 128 * mh + 32 * i + 8 * q + 4 * half;
+        const int row0 = rbase + (even ? 0 : 1);
+        const int row1 = rbase + (even ? 2 : 3);
+        if (row0 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row0) * words_per_shard_row + wcol] = w0;
+          if (PUSH)
+            box[static_cast<long long>(row0) * words_per_row + (r * shard >> 1) + wcol] =
+                w0 == kSentinel ? 0u : w0;
+        }
+        if (row1 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row1) * words_per_shard_row + wcol] = w1;
+          if (PUSH)
+            box[static_cast<long long>(row1) * words_per_row + (r * shard >> 1) + wcol] =
+                w1 == kSentinel ? 0u : w1;
+        }
+      }
+    }
+  }
+}
+
+template <int NT, int NCP>
 hipError_t launch_lmhead_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
                             uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s) {
   ShardTableN<NT> wt;
@@ -213,26 +418,283 @@ hipError_t launch_lmhead_nt(const u32x4 *x, const ShardTable &w, const OutTable 
     ot.p[r] = so.p[r];
   }
   const int vocab = tp * shard;
+  constexpr int kTN = 64 * NCP;
   const dim3 grid((vocab + kTN - 1) / kTN, (m + kTM - 1) / kTM);
+  const dim3 block(NCP * 128);
   if (box && keep)
-    hipLaunchKernelGGL((k_lmhead<NT, true, true>), grid, dim3(kThreads), 0, s, x, wt, ot, box, m,
+    hipLaunchKernelGGL((k_lmhead<NT, NCP, true, true>), grid, block, 0, s, x, wt, ot, box, m,
                        hidden, shard, vocab);
   else if (box)
-    hipLaunchKernelGGL((k_lmhead<NT, true, false>), grid, dim3(kThreads), 0, s, x, wt, ot, box, m,
+    hipLaunchKernelGGL((k_lmhead<NT, NCP, true, false>), grid, block, 0, s, x, wt, ot, box, m,
                        hidden, shard, vocab);
   else
-    hipLaunchKernelGGL((k_lmhead<NT, false, true>), grid, dim3(kThreads), 0, s, x, wt, ot, box, m,
+    hipLaunchKernelGGL((k_lmhead<NT, NCP, false, true>), grid, block, 0, s, x, wt, ot, box, m,
                        hidden, shard, vocab);
   return hipGetLastError();
+}
+
+template <int NCP>
+hipError_t launch_lmhead_ncp(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
+                             uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s) {
+  if (tp <= kSmallTable)
+    return launch_lmhead_nt<kSmallTable, NCP>(x, w, so, keep, box, m, hidden, shard, tp, s);
+  return launch_lmhead_nt<HG_MAX_TP, NCP>(x, w, so, keep, box, m, hidden, shard, tp, s);
+}
+
+// 64-wide K steps with separate pipeline depths for the two operands: X
+// (re-read by every workgroup, served from L2) in XS stages, the weights
+// (streamed once from HBM) in WS stages, filling the 160 KB of LDS with
+// XS=2, WS=3. X of step kb+XS-1 and weights of step kb+WS-1 are issued after
+// the barrier of step kb, X first, so that one wait for "all but the newest
+// weight step" covers both operands of step kb.
+template <int NT, int XS, int WS, bool PUSH, bool KEEP>
+__global__ __launch_bounds__(512) void k_lmhead_dma2(const u32x4 *x, ShardTableN<NT> w,
+                                                     OutTableN<NT> shards_out, uint32_t *box, int m,
+                                                     int hidden, int shard, int vocab) {
+  constexpr int KS = 64;
+  constexpr int kTN = 256;
+  constexpr int kRowBytes = 128;
+  constexpr int kSlots = 8;
+  constexpr int kRowsPerInst = 8;
+  constexpr int kPart = 256 * kRowBytes;  // one operand tile of one step: 32 KB
+  constexpr int kInst = 4;                // per operand, per wave, per step
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[(XS + WS) * kPart];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int mh = wave & 1;
+  const int nq = wave >> 1;
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int n0 = static_cast<int>(blockIdx.x) * kTN;
+  const int m0 = static_cast<int>(blockIdx.y) * kTM;
+  const int hv = hidden >> 3;
+  const int steps = (hidden + KS - 1) / KS;
+
+  // Instruction q of wave w fills rows 8*(8q+w) .. +8 of an operand tile.
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const u32x4 *xsrc[kInst], *wsrc[kInst];
+  bool xok[kInst], wok[kInst];
+  int seg[kInst];
+#pragma unroll
+  for (int q = 0; q < kInst; ++q) {
+    const int row = kRowsPerInst * (8 * q + wave) + lrow;  // 0..255
+    seg[q] = lslot ^ dswz<64>(row);
+    xok[q] = m0 + row < m;
+    xsrc[q] = x + static_cast<long long>(xok[q] ? m0 + row : 0) * hv;
+    const int n = n0 + row;
+    const int n_wave = __builtin_amdgcn_readfirstlane(n0 + kRowsPerInst * (8 * q + wave));
+    wok[q] = n < vocab;
+    const int r = n_wave < vocab ? n_wave / shard : 0;
+    wsrc[q] = w.p[r] + static_cast<long long>(wok[q] ? n - r * shard : 0) * hv;
+  }
+  unsigned char *xbase = lds;
+  unsigned char *wbase = lds + XS * kPart;
+  auto issue_x = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < kInst; ++q) {
+      const int kv = kb * kSlots + seg[q];
+      __builtin_amdgcn_global_load_lds(
+          xsrc[q] + (xok[q] && kv < hv ? kv : 0),
+          (__attribute__((address_space(3))) void *)(xbase + (kb % XS) * kPart +
+                                                     kRowsPerInst * (8 * q + wave) * kRowBytes),
+          16, 0, 0);
+    }
+  };
+  auto issue_w = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < kInst; ++q) {
+      const int kv = kb * kSlots + seg[q];
+      __builtin_amdgcn_global_load_lds(
+          wsrc[q] + (wok[q] && kv < hv ? kv : 0),
+          (__attribute__((address_space(3))) void *)(wbase + (kb % WS) * kPart +
+                                                     kRowsPerInst * (8 * q + wave) * kRowBytes),
+          16, 0, 2 /* nt */);
+    }
+  };
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[i][cb] = f32x16{};
+
+  const bool tails = hidden % KS != 0 || m0 + kTM > m;
+  // Prologue, in the order the steady state keeps: W(0..WS-2) then X(0..XS-2)
+  // interleaved so that X(kb) is always issued before W(kb+WS-2).
+  for (int p = 0; p < WS - 1 && p < steps; ++p) {
+    if (p < XS - 1) issue_x(p);
+    issue_w(p);
+  }
+  for (int kb = 0; kb < steps; ++kb) {
+    // Outstanding, oldest first: ..., X(kb), W(kb+1) [if issued]. Wait until
+    // only the newest weight step may remain.
+    if (WS >= 3 && kb + 1 < steps)
+      wait_vm<kInst>();
+    else
+      wait_vm<0>();
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+    unsigned char *sx = xbase + (kb % XS) * kPart;
+    unsigned char *sw = wbase + (kb % WS) * kPart;
+    if (tails) {
+#pragma unroll
+      for (int q = 0; q < kInst; ++q) {
+        const int kv = kb * kSlots + seg[q];
+        const int off = (kRowsPerInst * (8 * q + wave) + lrow) * kRowBytes + lslot * 16;
+        if (!(xok[q] && kv < hv)) *reinterpret_cast<u32x4 *>(sx + off) = u32x4{0u, 0u, 0u, 0u};
+        if (!(wok[q] && kv < hv)) *reinterpret_cast<u32x4 *>(sw + off) = u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (kb + XS - 1 < steps) issue_x(kb + XS - 1);
+    if (kb + WS - 1 < steps) issue_w(kb + WS - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = 4 * (j >> 1) + 2 * half + (j & 1);
+      bf16x8 b[2];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const int row = 64 * nq + 32 * cb + l32;
+        b[cb] = *reinterpret_cast<const bf16x8 *>(sw + row * kRowBytes + ((g ^ dswz<64>(row)) << 4));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 128 * mh + 32 * i + l32;
+        const bf16x8 a =
+            *reinterpret_cast<const bf16x8 *>(sx + row * kRowBytes + ((g ^ dswz<64>(row)) << 4));
+        acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[0], acc[i][0], 0, 0, 0);
+        acc[i][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[1], acc[i][1], 0, 0, 0);
+      }
+    }
+  }
+
+  const bool even = (l32 & 1) == 0;
+  const int words_per_shard_row = shard >> 1;
+  const int words_per_row = vocab >> 1;
+#pragma unroll
+  for (int cb = 0; cb < 2; ++cb) {
+    const int c0 = n0 + 64 * nq + 32 * cb;
+    if (c0 >= vocab) continue;
+    const int r = c0 / shard;
+    const int s_even = c0 - r * shard + (l32 & ~1);
+    const int wcol = s_even >> 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[t] = bf16_bits(acc[i][cb][4 * q + t]);
+        const uint32_t send = even ? (b[1] | (b[3] << 16)) : (b[0] | (b[2] << 16));
+        const uint32_t recv = swap_adjacent(send);
+        const uint32_t w0 = even ? (b[0] | (recv << 16)) : ((recv & 0xFFFFu) | (b[1] << 16));
+        const uint32_t w1 = even ? (b[2] | (recv & 0xFFFF0000u)) : ((recv >> 16) | (b[3] << 16));
+        const int rbase = m0 + 128 * mh + 32 * i + 8 * q + 4 * half;
+        const int row0 = rbase + (even ? 0 : 1);
+        const int row1 = rbase + (even ? 2 : 3);
+        if (row0 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row0) * words_per_shard_row + wcol] = w0;
+          if (PUSH)
+            box[static_cast<long long>(row0) * words_per_row + (r * shard >> 1) + wcol] =
+                w0 == kSentinel ? 0u : w0;
+        }
+        if (row1 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row1) * words_per_shard_row + wcol] = w1;
+          if (PUSH)
+            box[static_cast<long long>(row1) * words_per_row + (r * shard >> 1) + wcol] =
+                w1 == kSentinel ? 0u : w1;
+        }
+      }
+    }
+  }
+}
+
+template <int NT, int XS, int WS>
+hipError_t launch_lmhead_dma2_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
+                                 uint32_t *box, int m, int hidden, int shard, int tp,
+                                 hipStream_t s) {
+  ShardTableN<NT> wt;
+  OutTableN<NT> ot;
+  for (int r = 0; r < NT; ++r) {
+    wt.p[r] = w.p[r];
+    ot.p[r] = so.p[r];
+  }
+  const int vocab = tp * shard;
+  const dim3 grid((vocab + 255) / 256, (m + kTM - 1) / kTM);
+  if (box && keep)
+    hipLaunchKernelGGL((k_lmhead_dma2<NT, XS, WS, true, true>), grid, dim3(512), 0, s, x, wt, ot,
+                       box, m, hidden, shard, vocab);
+  else if (box)
+    hipLaunchKernelGGL((k_lmhead_dma2<NT, XS, WS, true, false>), grid, dim3(512), 0, s, x, wt, ot,
+                       box, m, hidden, shard, vocab);
+  else
+    hipLaunchKernelGGL((k_lmhead_dma2<NT, XS, WS, false, true>), grid, dim3(512), 0, s, x, wt, ot,
+                       box, m, hidden, shard, vocab);
+  return hipGetLastError();
+}
+
+template <int NT, int KS, int ST, bool WNT>
+hipError_t launch_lmhead_dma_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
+                                uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s) {
+  ShardTableN<NT> wt;
+  OutTableN<NT> ot;
+  for (int r = 0; r < NT; ++r) {
+    wt.p[r] = w.p[r];
+    ot.p[r] = so.p[r];
+  }
+  const int vocab = tp * shard;
+  const dim3 grid((vocab + 255) / 256, (m + kTM - 1) / kTM);
+  if (box && keep)
+    hipLaunchKernelGGL((k_lmhead_dma<NT, KS, ST, WNT, true, true>), grid, dim3(512), 0, s, x, wt,
+                       ot, box, m, hidden, shard, vocab);
+  else if (box)
+    hipLaunchKernelGGL((k_lmhead_dma<NT, KS, ST, WNT, true, false>), grid, dim3(512), 0, s, x, wt,
+                       ot, box, m, hidden, shard, vocab);
+  else
+    hipLaunchKernelGGL((k_lmhead_dma<NT, KS, ST, WNT, false, true>), grid, dim3(512), 0, s, x, wt,
+                       ot, box, m, hidden, shard, vocab);
+  return hipGetLastError();
+}
+
+template <int KS, int ST, bool WNT>
+hipError_t launch_lmhead_dma(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
+                             uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s) {
+  if (tp <= kSmallTable)
+    return launch_lmhead_dma_nt<kSmallTable, KS, ST, WNT>(x, w, so, keep, box, m, hidden, shard, tp,
+                                                          s);
+  return launch_lmhead_dma_nt<HG_MAX_TP, KS, ST, WNT>(x, w, so, keep, box, m, hidden, shard, tp, s);
 }
 
 }  // namespace
 
 hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &shards_out, bool keep,
-                         uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s) {
-  if (tp <= kSmallTable)
-    return launch_lmhead_nt<kSmallTable>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
-  return launch_lmhead_nt<HG_MAX_TP>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+                         uint32_t *box, int m, int hidden, int shard, int tp, int variant,
+                         hipStream_t s) {
+  switch (variant) {
+    case kGemmDirectLds:
+      return launch_lmhead_dma<32, 4, false>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+    case kGemmDirectLdsNt:
+      return launch_lmhead_dma<32, 4, true>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+    case kGemmDirectLds64:
+      return launch_lmhead_dma<64, 2, false>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+    case kGemmDirectLds64Nt:
+      return launch_lmhead_dma<64, 2, true>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+    case kGemmDirectLdsDeepW:
+      if (tp <= kSmallTable)
+        return launch_lmhead_dma2_nt<kSmallTable, 2, 3>(x, w, shards_out, keep, box, m, hidden,
+                                                         shard, tp, s);
+      return launch_lmhead_dma2_nt<HG_MAX_TP, 2, 3>(x, w, shards_out, keep, box, m, hidden, shard,
+                                                     tp, s);
+    case kGemmStaged256:
+      return launch_lmhead_ncp<4>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+    case kGemmStaged128:
+      return launch_lmhead_ncp<2>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+    default:
+      return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace hg

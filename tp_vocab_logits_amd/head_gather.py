@@ -92,7 +92,7 @@ def _weight_pointers(w, tp: int, shard: int, hidden: int) -> list[int]:
 
 
 def lmhead(x: torch.Tensor, w, tp: int, shard: int,
-           shards_out: torch.Tensor | None = None) -> torch.Tensor:
+           shards_out: torch.Tensor | None = None, variant: int = 0) -> torch.Tensor:
     """The lm_head shard product ``[TP, M, S] = X @ W_r^T`` per rank (BF16 in,
     fp32 accumulate, BF16 out), in the library's MFMA kernel."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
@@ -108,7 +108,7 @@ def lmhead(x: torch.Tensor, w, tp: int, shard: int,
     op = [shards_out.data_ptr() + r * step for r in range(tp)]
     with torch.cuda.device(x.device):
         check(lib().hg_lmhead(tp, shard, ctypes.c_void_p(x.data_ptr()), pointer_array(wp), hidden, m,
-                              pointer_array(op), _stream_handle(x.device)), "hg_lmhead")
+                              pointer_array(op), int(variant), _stream_handle(x.device)), "hg_lmhead")
     return shards_out
 
 
