@@ -182,8 +182,24 @@ int hg_lmhead(int tp, int shard, const void *x, const void *const *w, int hidden
 int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hidden, int m, void *out,
                    void *const *shards_out, void *stream);
 
-/* The parity the next served call will use (0 or 1), or HG_EINVAL. */
+/* The parity the next served call will use (0 or 1), or HG_EINVAL. With
+ * device-side parity on, this synchronises the device and reads the word. */
 int hg_parity(const hg_ctx *h);
+
+/*
+ * Keep the parity in device memory (enable = 1) or on the host (0, the
+ * default). Host-side parity cannot alternate when launches are replayed
+ * from a graph, which is why calls under graph capture are otherwise
+ * declined (API page, HeadGather class description and HeadGather.__call__
+ * source). With device-side parity each launch reads the parity word when it
+ * starts and the launch that completes a call (fused gather, collect) flips
+ * it when its last workgroup finishes, so calls captured into a graph --
+ * hg_gather, hg_push/hg_push_ranks + hg_collect, hg_gemm_gather -- are
+ * served and every replay alternates. Switching on copies the host parity to
+ * the device (stream-ordered); switching off waits for `stream` and copies it
+ * back. HG_ESTATE while a split push is pending; HG_EINVAL while capturing.
+ */
+int hg_set_device_parity(hg_ctx *h, int enable, void *stream);
 
 /* Read-only view of one parity of the mailbox, for inspection by tests:
  * *dev = device address of [cap][tp*shard] BF16, *bytes = its size. */

@@ -98,7 +98,8 @@ struct hg_ctx {
   int cus = 0;
   long long vv = 0;             // 16-byte vectors per mailbox / output row
   u32x4 *box = nullptr;         // [2][cap][vv]
-  unsigned *status = nullptr;   // poll-timeout counter (first word)
+  unsigned *status = nullptr;   // [0] poll timeouts, [1] finished workgroups, [2] parity word
+  bool dev_parity = false;      // parity kept in device memory (graph-capturable calls)
   int parity = 0;
   int pending_m = -1;           // split push awaiting its collect
   int pending_parity = 0;
@@ -109,6 +110,20 @@ struct hg_ctx {
   int fused_per_cu[4][4][3];
 
   u32x4 *parity_box(int p) const { return box + static_cast<long long>(p) * cap * vv; }
+  int *parity_word() const { return reinterpret_cast<int *>(status + 2); }
+  unsigned *done_word() const { return status + 1; }
+  // Parity selection of a launch: host parity `p` in host mode, the device
+  // word in device mode; `flip` on the launch that completes a call.
+  hg::ParityArg parity_arg(int p, bool flip) const {
+    hg::ParityArg pa;
+    pa.box = box;
+    pa.stride = static_cast<long long>(cap) * vv;
+    pa.dev = dev_parity ? parity_word() : nullptr;
+    pa.done = done_word();
+    pa.p = p;
+    pa.flip = flip ? 1 : 0;
+    return pa;
+  }
   size_t row_bytes() const { return static_cast<size_t>(vv) * 16; }
 };
 
@@ -218,7 +233,8 @@ int check_call(hg_ctx *h, const void *const *shards, int m, unsigned long long r
   }
   if (m == 0 || m > h->cap) return HG_EDECLINE;
   const int cs = capture_state(static_cast<hipStream_t>(stream));
-  if (cs != HG_OK) return cs;
+  if (cs < 0) return cs;
+  if (cs == HG_EDECLINE && !h->dev_parity) return HG_EDECLINE;  // host parity cannot be replayed
   int rc = check_device(h);
   if (rc != HG_OK) return rc;
   const size_t out_bytes = static_cast<size_t>(m) * h->row_bytes();
@@ -299,8 +315,8 @@ HG_API int hg_arm(hg_ctx *h, void *stream) {
   const int block = 256;
   long long grid = (vectors + block - 1) / block;
   if (grid > static_cast<long long>(h->cus) * 8) grid = static_cast<long long>(h->cus) * 8;
-  HIP_TRY(hg::launch_arm(h->box, vectors, static_cast<int>(grid), block,
-                         static_cast<hipStream_t>(stream)));
+  HIP_TRY(hg::launch_arm(h->box, vectors, h->parity_word(), h->done_word(), static_cast<int>(grid),
+                         block, static_cast<hipStream_t>(stream)));
   h->parity = 0;
   h->pending_m = -1;
   h->pending_ranks = 0;
@@ -325,10 +341,10 @@ HG_API int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, voi
   if (want < lim) lim = want;
   if (lim < 1) return HG_EINVAL;
   const int grid = static_cast<int>(tiles < lim ? tiles : lim);
-  HIP_TRY(hg::launch_fused(table, g, md, h->parity_box(h->parity), used_box_bytes(h, m),
+  HIP_TRY(hg::launch_fused(table, g, md, h->parity_arg(h->parity, true), used_box_bytes(h, m),
                            static_cast<u32x4 *>(out), h->status, h->poll_limit, h->tune.poll_skew,
                            grid, h->tune.fused_block, static_cast<hipStream_t>(stream)));
-  h->parity ^= 1;
+  if (!h->dev_parity) h->parity ^= 1;
   return HG_OK;
 }
 
@@ -341,8 +357,8 @@ HG_API int hg_push_ranks(hg_ctx *h, const void *const *shards, int m, unsigned l
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, vpt);
   const int block = h->tune.split_block;
   const int p = h->pending_m >= 0 ? h->pending_parity : h->parity;
-  HIP_TRY(hg::launch_push(table, g, vpt, h->parity_box(p), ranks, split_grid(h, g, block), block,
-                          static_cast<hipStream_t>(stream)));
+  HIP_TRY(hg::launch_push(table, g, vpt, h->parity_arg(p, false), ranks, split_grid(h, g, block),
+                          block, static_cast<hipStream_t>(stream)));
   h->pending_m = m;
   h->pending_parity = p;
   h->pending_ranks |= ranks;
@@ -359,7 +375,8 @@ HG_API int hg_collect(hg_ctx *h, int m, void *out, void *stream) {
   if (!h || m < 0) return HG_EINVAL;
   if (h->pending_m < 0 || h->pending_m != m) return HG_ESTATE;
   const int cs = capture_state(static_cast<hipStream_t>(stream));
-  if (cs != HG_OK) return cs;
+  if (cs < 0) return cs;
+  if (cs == HG_EDECLINE && !h->dev_parity) return HG_EDECLINE;
   int rc = check_device(h);
   if (rc != HG_OK) return rc;
   const size_t out_bytes = static_cast<size_t>(m) * h->row_bytes();
@@ -368,12 +385,12 @@ HG_API int hg_collect(hg_ctx *h, int m, void *out, void *stream) {
   const hg::Modes md = pick_modes(h, h->tune.split_vpt, m);
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
   const int block = h->tune.split_block;
-  HIP_TRY(hg::launch_collect(g, md, h->parity_box(h->pending_parity), used_box_bytes(h, m),
+  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->pending_parity, true), used_box_bytes(h, m),
                              static_cast<u32x4 *>(out), h->status, h->poll_limit,
                              split_grid(h, g, block), block, static_cast<hipStream_t>(stream)));
   h->pending_m = -1;
   h->pending_ranks = 0;
-  h->parity = h->pending_parity ^ 1;
+  if (!h->dev_parity) h->parity = h->pending_parity ^ 1;
   return HG_OK;
 }
 
@@ -441,8 +458,9 @@ HG_API int hg_lmhead(int tp, int shard, const void *x, const void *const *w, int
   const int rc = check_lmhead(tp, shard, x, w, hidden, m, shards_out, &wt, &ot);
   if (rc != HG_OK) return rc;
   if (m == 0) return HG_OK;
-  HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, true, nullptr, m, hidden, shard,
-                            tp, variant ? variant : kDefaultGemmVariant,
+  hg::ParityArg none = {};
+  HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, true, false, none, m, hidden,
+                            shard, tp, variant ? variant : kDefaultGemmVariant,
                             static_cast<hipStream_t>(stream)));
   return HG_OK;
 }
@@ -453,7 +471,8 @@ HG_API int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hi
   if (h->pending_m >= 0) return HG_ESTATE;
   if (m == 0 || m > h->cap) return HG_EDECLINE;
   const int cs = capture_state(static_cast<hipStream_t>(stream));
-  if (cs != HG_OK) return cs;
+  if (cs < 0) return cs;
+  if (cs == HG_EDECLINE && !h->dev_parity) return HG_EDECLINE;
   int rc = check_device(h);
   if (rc != HG_OK) return rc;
   ShardTable wt;
@@ -466,20 +485,50 @@ HG_API int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hi
       overlaps(out, out_bytes, x, static_cast<size_t>(m) * hidden * 2))
     return HG_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  u32x4 *box = h->parity_box(h->parity);
-  HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, shards_out != nullptr,
-                            reinterpret_cast<uint32_t *>(box), m, hidden, h->shard, h->tp,
+  HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, shards_out != nullptr, true,
+                            h->parity_arg(h->parity, false), m, hidden, h->shard, h->tp,
                             h->tune.gemm_variant ? h->tune.gemm_variant : kDefaultGemmVariant, s));
   const hg::Modes md = pick_modes(h, h->tune.split_vpt, m);
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
   const int block = h->tune.split_block;
-  HIP_TRY(hg::launch_collect(g, md, box, used_box_bytes(h, m), static_cast<u32x4 *>(out),
-                             h->status, h->poll_limit, split_grid(h, g, block), block, s));
-  h->parity ^= 1;
+  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->parity, true), used_box_bytes(h, m),
+                             static_cast<u32x4 *>(out), h->status, h->poll_limit,
+                             split_grid(h, g, block), block, s));
+  if (!h->dev_parity) h->parity ^= 1;
   return HG_OK;
 }
 
-HG_API int hg_parity(const hg_ctx *h) { return h ? h->parity : HG_EINVAL; }
+HG_API int hg_parity(const hg_ctx *h) {
+  if (!h) return HG_EINVAL;
+  if (!h->dev_parity) return h->parity;
+  int v = -1;
+  HIP_TRY(hipDeviceSynchronize());
+  HIP_TRY(hipMemcpy(&v, h->parity_word(), sizeof v, hipMemcpyDeviceToHost));
+  return v;
+}
+
+HG_API int hg_set_device_parity(hg_ctx *h, int enable, void *stream) {
+  if (!h || (enable != 0 && enable != 1)) return HG_EINVAL;
+  if (h->pending_m >= 0) return HG_ESTATE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int cs = capture_state(s);
+  if (cs == HG_EDECLINE) return HG_EINVAL;  // not while capturing
+  if (cs != HG_OK) return cs;
+  int rc = check_device(h);
+  if (rc != HG_OK) return rc;
+  if (enable && !h->dev_parity) {
+    HIP_TRY(hg::launch_set_word(h->parity_word(), h->parity, s));
+    HIP_TRY(hg::launch_set_word(reinterpret_cast<int *>(h->done_word()), 0, s));
+    h->dev_parity = true;
+  } else if (!enable && h->dev_parity) {
+    int v = 0;
+    HIP_TRY(hipMemcpyAsync(&v, h->parity_word(), sizeof v, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipStreamSynchronize(s));
+    h->parity = v & 1;
+    h->dev_parity = false;
+  }
+  return HG_OK;
+}
 
 HG_API int hg_mailbox(const hg_ctx *h, int parity, const void **dev, size_t *bytes) {
   if (!h || (parity != 0 && parity != 1) || !dev || !bytes) return HG_EINVAL;

@@ -69,21 +69,46 @@ struct Modes {
   int rearm_stream;  // re-arm with non-temporal stores (1) or plain stores (0)
 };
 
+// Which mailbox parity a launch uses. Host mode (`dev` null): parity `p`,
+// chosen by the host. Device mode: the launch reads the parity from *dev when
+// it starts and, if `flip`, the last of its workgroups to finish writes the
+// other parity back (finished workgroups are counted in *done). Device mode
+// keeps the alternation right when launches are replayed from a graph.
+struct ParityArg {
+  u32x4 *box;        // row 0 of parity 0; parity p starts at box + p * stride
+  long long stride;  // 16-byte vectors per parity
+  int *dev;          // device parity word, or null
+  unsigned *done;    // finished-workgroup counter (device mode)
+  int p;             // host-mode parity
+  int flip;          // this launch completes a call (fused gather, collect)
+};
+
+// Parity of a launch (device code).
+__device__ __forceinline__ int launch_parity(const ParityArg &pa) {
+  if (!pa.dev) return pa.p;
+  return __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(pa.dev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // Builds the geometry for m rows at `vpt` vectors per lane.
 Geometry make_geometry(int tp, int shard, int m, int vpt);
 
 // Kernel launchers. Each returns the launch status (hipGetLastError).
 // `box_bytes` is the size of the mailbox rows in use from `box` on (it bounds
 // the 128-bit coherent accesses, which use 32-bit offsets).
-hipError_t launch_arm(u32x4 *box, long long vectors, int grid, int block, hipStream_t s);
-hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md, u32x4 *box,
-                        unsigned box_bytes, u32x4 *out, unsigned *status, unsigned long long limit,
-                        int skew, int grid, int block, hipStream_t s);
-hipError_t launch_push(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *box,
+// launch_arm also zeroes *pdev and *done when they are non-null.
+hipError_t launch_arm(u32x4 *box, long long vectors, int *pdev, unsigned *done, int grid, int block,
+                      hipStream_t s);
+// *word := value (one thread).
+hipError_t launch_set_word(int *word, int value, hipStream_t s);
+hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md,
+                        const ParityArg &pa, unsigned box_bytes, u32x4 *out, unsigned *status,
+                        unsigned long long limit, int skew, int grid, int block, hipStream_t s);
+hipError_t launch_push(const ShardTable &sh, const Geometry &g, int vpt, const ParityArg &pa,
                        unsigned long long ranks, int grid, int block, hipStream_t s);
-hipError_t launch_collect(const Geometry &g, const Modes &md, u32x4 *box, unsigned box_bytes,
-                          u32x4 *out, unsigned *status, unsigned long long limit, int grid,
-                          int block, hipStream_t s);
+hipError_t launch_collect(const Geometry &g, const Modes &md, const ParityArg &pa,
+                          unsigned box_bytes, u32x4 *out, unsigned *status,
+                          unsigned long long limit, int grid, int block, hipStream_t s);
 hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *out, int grid,
                         int block, hipStream_t s);
 
@@ -102,9 +127,10 @@ enum GemmVariant : int {
   kGemmDirectLds64Nt = 6,  // as 5, weight loads non-temporal
   kGemmDirectLdsDeepW = 7,  // 64-wide K steps, 2 X stages + 3 weight stages, weights nt
 };
+// `box` (when `push`) selects the mailbox rows through a ParityArg.
 hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &shards_out, bool keep,
-                         uint32_t *box, int m, int hidden, int shard, int tp, int variant,
-                         hipStream_t s);
+                         bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
+                         int variant, hipStream_t s);
 
 // Resident workgroups per CU of the fused kernel variant at a block size.
 hipError_t fused_blocks_per_cu(const Modes &md, int tp, int block, int *blocks);

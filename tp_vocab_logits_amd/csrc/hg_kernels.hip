@@ -242,6 +242,23 @@ __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane
   }
 }
 
+// Device mode, completing launch: the last workgroup to finish flips the
+// parity word for the next launch on the stream. Every workgroup read the
+// parity before it counts itself here.
+__device__ __forceinline__ void finish_parity(const ParityArg &pa, int p) {
+  if (!pa.dev || !pa.flip) return;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned total = gridDim.x * gridDim.y * gridDim.z;
+    const unsigned old = __hip_atomic_fetch_add(pa.done, 1u, __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+    if (old == total - 1) {
+      __hip_atomic_store(pa.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(pa.dev, p ^ 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
 }
@@ -254,8 +271,13 @@ __device__ __forceinline__ int waves_per_block() { return static_cast<int>(block
 // Kernels
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(1024) void k_arm(u32x4 *box, long long vectors) {
+__global__ __launch_bounds__(1024) void k_arm(u32x4 *box, long long vectors, int *pdev,
+                                              unsigned *done) {
   const u32x4 armed = {kSentinel, kSentinel, kSentinel, kSentinel};
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    if (pdev) *pdev = 0;
+    if (done) *done = 0u;
+  }
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
   for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < vectors;
        i += stride)
@@ -272,10 +294,12 @@ __global__ __launch_bounds__(1024) void k_arm(u32x4 *box, long long vectors) {
 // only the first `skew` workgroups wait on a higher-numbered one; every other
 // wait is on a workgroup dispatched earlier.
 template <int VPT, int PUSH, int POLL, int NT>
-__global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, u32x4 *box_ptr,
+__global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, ParityArg pa,
                                                 unsigned box_bytes, u32x4 *out, unsigned *status,
                                                 unsigned long long limit, int skew,
                                                 int rearm_stream) {
+  const int p = launch_parity(pa);
+  u32x4 *box_ptr = pa.box + p * pa.stride;
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
@@ -297,13 +321,15 @@ __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, 
     const int c = t * waves + wave;
     if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud, rearm_stream);
   }
+  finish_parity(pa, p);
 }
 
 // Split variant, first half: the push alone, by the ranks whose bit is set in
 // `ranks` (visible to the next kernel on the stream at kernel end).
 template <int VPT, int NT>
-__global__ __launch_bounds__(1024) void k_push(ShardTableN<NT> sh, Geometry g, u32x4 *box_ptr,
+__global__ __launch_bounds__(1024) void k_push(ShardTableN<NT> sh, Geometry g, ParityArg pa,
                                                unsigned long long ranks) {
+  u32x4 *box_ptr = pa.box + launch_parity(pa) * pa.stride;
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
@@ -319,9 +345,11 @@ __global__ __launch_bounds__(1024) void k_push(ShardTableN<NT> sh, Geometry g, u
 
 // Split variant, second half: poll, copy, re-arm.
 template <int VPT, int POLL>
-__global__ __launch_bounds__(1024) void k_collect(Geometry g, u32x4 *box_ptr, unsigned box_bytes,
+__global__ __launch_bounds__(1024) void k_collect(Geometry g, ParityArg pa, unsigned box_bytes,
                                                   u32x4 *out, unsigned *status,
                                                   unsigned long long limit, int rearm_stream) {
+  const int p = launch_parity(pa);
+  u32x4 *box_ptr = pa.box + p * pa.stride;
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
@@ -332,7 +360,10 @@ __global__ __launch_bounds__(1024) void k_collect(Geometry g, u32x4 *box_ptr, un
     const int c = t * waves + wave;
     if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud, rearm_stream);
   }
+  finish_parity(pa, p);
 }
+
+__global__ void k_set_word(int *word, int value) { *word = value; }
 
 // The stock path's single-device share: rank-order concatenation, bytes
 // unchanged.
@@ -409,21 +440,27 @@ Geometry make_geometry(int tp, int shard, int m, int vpt) {
   return g;
 }
 
-hipError_t launch_arm(u32x4 *box, long long vectors, int grid, int block, hipStream_t s) {
-  hipLaunchKernelGGL(k_arm, dim3(grid), dim3(block), 0, s, box, vectors);
+hipError_t launch_arm(u32x4 *box, long long vectors, int *pdev, unsigned *done, int grid, int block,
+                      hipStream_t s) {
+  hipLaunchKernelGGL(k_arm, dim3(grid), dim3(block), 0, s, box, vectors, pdev, done);
   return hipGetLastError();
 }
 
-hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md, u32x4 *box,
-                        unsigned box_bytes, u32x4 *out, unsigned *status, unsigned long long limit,
-                        int skew, int grid, int block, hipStream_t s) {
+hipError_t launch_set_word(int *word, int value, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_word, dim3(1), dim3(1), 0, s, word, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md,
+                        const ParityArg &pa, unsigned box_bytes, u32x4 *out, unsigned *status,
+                        unsigned long long limit, int skew, int grid, int block, hipStream_t s) {
   return by_table(sh, g.tp, [&](const auto &t) {
     constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
     return by_vpt(md.vpt, [&](auto v) {
       return by_push(md.push, [&](auto pu) {
         return by_poll(md.poll, [&](auto po) {
           constexpr int V = decltype(v)::value, PU = decltype(pu)::value, PO = decltype(po)::value;
-          hipLaunchKernelGGL((k_fused<V, PU, PO, NT>), dim3(grid), dim3(block), 0, s, t, g, box,
+          hipLaunchKernelGGL((k_fused<V, PU, PO, NT>), dim3(grid), dim3(block), 0, s, t, g, pa,
                              box_bytes, out, status, limit, skew, md.rearm_stream);
           return hipGetLastError();
         });
@@ -432,25 +469,25 @@ hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md
   });
 }
 
-hipError_t launch_push(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *box,
+hipError_t launch_push(const ShardTable &sh, const Geometry &g, int vpt, const ParityArg &pa,
                        unsigned long long ranks, int grid, int block, hipStream_t s) {
   return by_table(sh, g.tp, [&](const auto &t) {
     constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
     return by_vpt(vpt, [&](auto v) {
       constexpr int V = decltype(v)::value;
-      hipLaunchKernelGGL((k_push<V, NT>), dim3(grid), dim3(block), 0, s, t, g, box, ranks);
+      hipLaunchKernelGGL((k_push<V, NT>), dim3(grid), dim3(block), 0, s, t, g, pa, ranks);
       return hipGetLastError();
     });
   });
 }
 
-hipError_t launch_collect(const Geometry &g, const Modes &md, u32x4 *box, unsigned box_bytes,
-                          u32x4 *out, unsigned *status, unsigned long long limit, int grid,
-                          int block, hipStream_t s) {
+hipError_t launch_collect(const Geometry &g, const Modes &md, const ParityArg &pa,
+                          unsigned box_bytes, u32x4 *out, unsigned *status,
+                          unsigned long long limit, int grid, int block, hipStream_t s) {
   return by_vpt(md.vpt, [&](auto v) {
     return by_poll(md.poll, [&](auto po) {
       constexpr int V = decltype(v)::value, PO = decltype(po)::value;
-      hipLaunchKernelGGL((k_collect<V, PO>), dim3(grid), dim3(block), 0, s, g, box, box_bytes, out,
+      hipLaunchKernelGGL((k_collect<V, PO>), dim3(grid), dim3(block), 0, s, g, pa, box_bytes, out,
                          status, limit, md.rearm_stream);
       return hipGetLastError();
     });

@@ -56,7 +56,7 @@ __device__ __forceinline__ uint32_t swap_adjacent(uint32_t v) {
 
 template <int NT, int NCP, bool PUSH, bool KEEP>
 __global__ __launch_bounds__(NCP * 128) void k_lmhead(const u32x4 *x, ShardTableN<NT> w,
-                                                      OutTableN<NT> shards_out, uint32_t *box,
+                                                      OutTableN<NT> shards_out, ParityArg pa,
                                                       int m, int hidden, int shard, int vocab) {
   constexpr int kThreads = NCP * 128;
   constexpr int kTN = 64 * NCP;
@@ -177,6 +177,8 @@ __global__ __launch_bounds__(NCP * 128) void k_lmhead(const u32x4 *x, ShardTable
   const bool even = (l32 & 1) == 0;
   const int words_per_shard_row = shard >> 1;
   const int words_per_row = vocab >> 1;
+  uint32_t *box = PUSH ? reinterpret_cast<uint32_t *>(pa.box + launch_parity(pa) * pa.stride)
+                       : nullptr;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int c0 = n0 + 64 * nq + 32 * cb;
@@ -240,7 +242,7 @@ __device__ __forceinline__ void wait_vm() {
 
 template <int NT, int KS, int ST, bool WNT, bool PUSH, bool KEEP>
 __global__ __launch_bounds__(512) void k_lmhead_dma(const u32x4 *x, ShardTableN<NT> w,
-                                                    OutTableN<NT> shards_out, uint32_t *box, int m,
+                                                    OutTableN<NT> shards_out, ParityArg pa, int m,
                                                     int hidden, int shard, int vocab) {
   constexpr int kTN = 256;
   constexpr int kRowBytes = KS * 2;
@@ -370,6 +372,8 @@ __global__ __launch_bounds__(512) void k_lmhead_dma(const u32x4 *x, ShardTableN<
   const bool even = (l32 & 1) == 0;
   const int words_per_shard_row = shard >> 1;
   const int words_per_row = vocab >> 1;
+  uint32_t *box = PUSH ? reinterpret_cast<uint32_t *>(pa.box + launch_parity(pa) * pa.stride)
+                       : nullptr;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int c0 = n0 + 64 * nq + 32 * cb;
@@ -410,7 +414,8 @@ __global__ __launch_bounds__(512) void k_lmhead_dma(const u32x4 *x, ShardTableN<
 
 template <int NT, int NCP>
 hipError_t launch_lmhead_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
-                            uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s) {
+                            bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
+                            hipStream_t s) {
   ShardTableN<NT> wt;
   OutTableN<NT> ot;
   for (int r = 0; r < NT; ++r) {
@@ -421,10 +426,10 @@ hipError_t launch_lmhead_nt(const u32x4 *x, const ShardTable &w, const OutTable 
   constexpr int kTN = 64 * NCP;
   const dim3 grid((vocab + kTN - 1) / kTN, (m + kTM - 1) / kTM);
   const dim3 block(NCP * 128);
-  if (box && keep)
+  if (push && keep)
     hipLaunchKernelGGL((k_lmhead<NT, NCP, true, true>), grid, block, 0, s, x, wt, ot, box, m,
                        hidden, shard, vocab);
-  else if (box)
+  else if (push)
     hipLaunchKernelGGL((k_lmhead<NT, NCP, true, false>), grid, block, 0, s, x, wt, ot, box, m,
                        hidden, shard, vocab);
   else
@@ -435,10 +440,11 @@ hipError_t launch_lmhead_nt(const u32x4 *x, const ShardTable &w, const OutTable 
 
 template <int NCP>
 hipError_t launch_lmhead_ncp(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
-                             uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s) {
+                             bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
+                             hipStream_t s) {
   if (tp <= kSmallTable)
-    return launch_lmhead_nt<kSmallTable, NCP>(x, w, so, keep, box, m, hidden, shard, tp, s);
-  return launch_lmhead_nt<HG_MAX_TP, NCP>(x, w, so, keep, box, m, hidden, shard, tp, s);
+    return launch_lmhead_nt<kSmallTable, NCP>(x, w, so, keep, push, box, m, hidden, shard, tp, s);
+  return launch_lmhead_nt<HG_MAX_TP, NCP>(x, w, so, keep, push, box, m, hidden, shard, tp, s);
 }
 
 // 64-wide K steps with separate pipeline depths for the two operands: X
@@ -449,7 +455,7 @@ hipError_t launch_lmhead_ncp(const u32x4 *x, const ShardTable &w, const OutTable
 // weight step" covers both operands of step kb.
 template <int NT, int XS, int WS, bool PUSH, bool KEEP>
 __global__ __launch_bounds__(512) void k_lmhead_dma2(const u32x4 *x, ShardTableN<NT> w,
-                                                     OutTableN<NT> shards_out, uint32_t *box, int m,
+                                                     OutTableN<NT> shards_out, ParityArg pa, int m,
                                                      int hidden, int shard, int vocab) {
   constexpr int KS = 64;
   constexpr int kTN = 256;
@@ -574,6 +580,8 @@ __global__ __launch_bounds__(512) void k_lmhead_dma2(const u32x4 *x, ShardTableN
   const bool even = (l32 & 1) == 0;
   const int words_per_shard_row = shard >> 1;
   const int words_per_row = vocab >> 1;
+  uint32_t *box = PUSH ? reinterpret_cast<uint32_t *>(pa.box + launch_parity(pa) * pa.stride)
+                       : nullptr;
 #pragma unroll
   for (int cb = 0; cb < 2; ++cb) {
     const int c0 = n0 + 64 * nq + 32 * cb;
@@ -614,8 +622,8 @@ __global__ __launch_bounds__(512) void k_lmhead_dma2(const u32x4 *x, ShardTableN
 
 template <int NT, int XS, int WS>
 hipError_t launch_lmhead_dma2_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
-                                 uint32_t *box, int m, int hidden, int shard, int tp,
-                                 hipStream_t s) {
+                                 bool push, const ParityArg &box, int m, int hidden, int shard,
+                                 int tp, hipStream_t s) {
   ShardTableN<NT> wt;
   OutTableN<NT> ot;
   for (int r = 0; r < NT; ++r) {
@@ -624,10 +632,10 @@ hipError_t launch_lmhead_dma2_nt(const u32x4 *x, const ShardTable &w, const OutT
   }
   const int vocab = tp * shard;
   const dim3 grid((vocab + 255) / 256, (m + kTM - 1) / kTM);
-  if (box && keep)
+  if (push && keep)
     hipLaunchKernelGGL((k_lmhead_dma2<NT, XS, WS, true, true>), grid, dim3(512), 0, s, x, wt, ot,
                        box, m, hidden, shard, vocab);
-  else if (box)
+  else if (push)
     hipLaunchKernelGGL((k_lmhead_dma2<NT, XS, WS, true, false>), grid, dim3(512), 0, s, x, wt, ot,
                        box, m, hidden, shard, vocab);
   else
@@ -638,7 +646,8 @@ hipError_t launch_lmhead_dma2_nt(const u32x4 *x, const ShardTable &w, const OutT
 
 template <int NT, int KS, int ST, bool WNT>
 hipError_t launch_lmhead_dma_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
-                                uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s) {
+                                bool push, const ParityArg &box, int m, int hidden, int shard,
+                                int tp, hipStream_t s) {
   ShardTableN<NT> wt;
   OutTableN<NT> ot;
   for (int r = 0; r < NT; ++r) {
@@ -647,10 +656,10 @@ hipError_t launch_lmhead_dma_nt(const u32x4 *x, const ShardTable &w, const OutTa
   }
   const int vocab = tp * shard;
   const dim3 grid((vocab + 255) / 256, (m + kTM - 1) / kTM);
-  if (box && keep)
+  if (push && keep)
     hipLaunchKernelGGL((k_lmhead_dma<NT, KS, ST, WNT, true, true>), grid, dim3(512), 0, s, x, wt,
                        ot, box, m, hidden, shard, vocab);
-  else if (box)
+  else if (push)
     hipLaunchKernelGGL((k_lmhead_dma<NT, KS, ST, WNT, true, false>), grid, dim3(512), 0, s, x, wt,
                        ot, box, m, hidden, shard, vocab);
   else
@@ -661,37 +670,39 @@ hipError_t launch_lmhead_dma_nt(const u32x4 *x, const ShardTable &w, const OutTa
 
 template <int KS, int ST, bool WNT>
 hipError_t launch_lmhead_dma(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
-                             uint32_t *box, int m, int hidden, int shard, int tp, hipStream_t s) {
+                             bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
+                             hipStream_t s) {
   if (tp <= kSmallTable)
-    return launch_lmhead_dma_nt<kSmallTable, KS, ST, WNT>(x, w, so, keep, box, m, hidden, shard, tp,
-                                                          s);
-  return launch_lmhead_dma_nt<HG_MAX_TP, KS, ST, WNT>(x, w, so, keep, box, m, hidden, shard, tp, s);
+    return launch_lmhead_dma_nt<kSmallTable, KS, ST, WNT>(x, w, so, keep, push, box, m, hidden,
+                                                          shard, tp, s);
+  return launch_lmhead_dma_nt<HG_MAX_TP, KS, ST, WNT>(x, w, so, keep, push, box, m, hidden, shard,
+                                                      tp, s);
 }
 
 }  // namespace
 
 hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &shards_out, bool keep,
-                         uint32_t *box, int m, int hidden, int shard, int tp, int variant,
-                         hipStream_t s) {
+                         bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
+                         int variant, hipStream_t s) {
   switch (variant) {
     case kGemmDirectLds:
-      return launch_lmhead_dma<32, 4, false>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+      return launch_lmhead_dma<32, 4, false>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmDirectLdsNt:
-      return launch_lmhead_dma<32, 4, true>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+      return launch_lmhead_dma<32, 4, true>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmDirectLds64:
-      return launch_lmhead_dma<64, 2, false>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+      return launch_lmhead_dma<64, 2, false>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmDirectLds64Nt:
-      return launch_lmhead_dma<64, 2, true>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+      return launch_lmhead_dma<64, 2, true>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmDirectLdsDeepW:
       if (tp <= kSmallTable)
-        return launch_lmhead_dma2_nt<kSmallTable, 2, 3>(x, w, shards_out, keep, box, m, hidden,
-                                                         shard, tp, s);
-      return launch_lmhead_dma2_nt<HG_MAX_TP, 2, 3>(x, w, shards_out, keep, box, m, hidden, shard,
-                                                     tp, s);
+        return launch_lmhead_dma2_nt<kSmallTable, 2, 3>(x, w, shards_out, keep, push, box, m,
+                                                         hidden, shard, tp, s);
+      return launch_lmhead_dma2_nt<HG_MAX_TP, 2, 3>(x, w, shards_out, keep, push, box, m, hidden,
+                                                     shard, tp, s);
     case kGemmStaged256:
-      return launch_lmhead_ncp<4>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+      return launch_lmhead_ncp<4>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmStaged128:
-      return launch_lmhead_ncp<2>(x, w, shards_out, keep, box, m, hidden, shard, tp, s);
+      return launch_lmhead_ncp<2>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     default:
       return hipErrorInvalidValue;
   }

@@ -251,6 +251,13 @@ class HeadGather:
                                         _stream_handle(self.device)), "hg_copy_mailbox")
         return dst
 
+    def set_device_parity(self, enable: bool) -> None:
+        """Keep the parity in device memory so calls can be captured into a
+        graph and replayed (see ``hg_set_device_parity``)."""
+        with torch.cuda.device(self.device):
+            check(lib().hg_set_device_parity(self._h, 1 if enable else 0, _stream_handle(self.device)),
+                  "hg_set_device_parity")
+
     def set_poll_limit(self, spins: int) -> None:
         check(lib().hg_set_poll_limit(self._h, int(spins)), "hg_set_poll_limit")
 
