@@ -57,6 +57,8 @@ def parse_args():
     ap.add_argument("--variant", choices=["fused", "split"], default="fused")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--pmc-probe", action="store_true")
+    ap.add_argument("--no-graph", dest="graph", action="store_false",
+                    help="skip the graph-replay leg of the M=1 decode gather")
     ap.add_argument("--producer-steps", type=int, default=10,
                     help="timed M=256 lm_head producer + gather calls (0: skip)")
     return ap.parse_args()
@@ -168,6 +170,30 @@ def main() -> int:
         raise _lib.HgError(-abs(rcs), "timed decode loop")
     us_m1 = t_dec.ms * 1000.0 / args.steps
 
+    # ---------------- decode, captured: the same K gathers replayed from a graph
+    # (parity kept in device memory so that every replay alternates it)
+    us_graph = None
+    if args.variant == "fused" and args.graph:
+        hg_g = HeadGather(wd.tp, wd.shard, wd.cap, device=dev)
+        hg_g.set_device_parity(True)
+        g_outs = torch.empty((n_out, wd.rows, wd.vocab), dtype=torch.bfloat16, device=dev)
+        g_ptrs = [ctypes.c_void_p(g_outs[n].data_ptr()) for n in range(n_out)]
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            gs = ctypes.c_void_p(side.cuda_stream)
+            for n in range(args.steps):
+                rcs |= lib.hg_gather(hg_g.handle, dec_ptrs[n % wd.pool], wd.rows, g_ptrs[n], gs)
+        if rcs:
+            raise _lib.HgError(-abs(rcs), "graph capture")
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"decode graph replay of {args.steps} captured gathers")
+        with Timer(torch, stream) as t_g:
+            graph.replay()
+        us_graph = t_g.ms * 1000.0 / args.steps
+
     # ---------------- M=256 gather: cold (rotating) and back-to-back -------
     fn_big = call_fn(hg_big, args.variant)
     for n in range(6):
@@ -247,6 +273,14 @@ def main() -> int:
         if not torch.equal(hg_big.mailbox(p).view(torch.int32), armed_big):
             log("FAIL: M=256 mailbox not all-sentinel after the run")
             return 1
+    if us_graph is not None:
+        for p in (0, 1):
+            if not torch.equal(hg_g.mailbox(p).view(torch.int32), armed):
+                log("FAIL: graph-replayed decode mailbox not all-sentinel")
+                return 1
+        if hg_g.parity != 0 or hg_g.poll_status() != _lib.HG_OK:  # 2 replays of K calls: even
+            log("FAIL: device parity after the graph replays")
+            return 1
     if hg.poll_status() != _lib.HG_OK or hg_big.poll_status() != _lib.HG_OK:
         log("FAIL: a bounded poll gave up")
         return 1
@@ -286,6 +320,12 @@ def main() -> int:
             if not np.array_equal(got[k], want_dec[k]):
                 log(f"FAIL: decode output of call {k} differs from the oracle")
                 return 1
+        if us_graph is not None:
+            got = g_outs[: wd.pool].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            for k in range(min(wd.pool, args.steps)):
+                if not np.array_equal(got[k], want_dec[k]):
+                    log(f"FAIL: graph-replayed decode output of call {k} differs from the oracle")
+                    return 1
         if not np.array_equal(syn.from_torch_bf16(big_out[0]), want_big):
             log("FAIL: M=256 output differs from the oracle")
             return 1
@@ -337,6 +377,10 @@ def main() -> int:
                                "M=1, cap=8, back-to-back calls on one stream, inputs resident",
                    "variant": args.variant, "tp": wd.tp, "vocab": wd.vocab, "rows": wd.rows,
                    "cap": wd.cap},
+        "decode_graph": None if us_graph is None else {
+            "workload": "the same M=1 decode gathers captured into one HIP graph "
+                        "(device-side parity) and replayed",
+            "us_per_gather": round(us_graph, 3), "gathers_per_replay": args.steps},
         "large_m": {"workload": "gather TP=8, V=163840, M=256, cap=256, 3 rotating buffer sets",
                     "us_per_gather_cold": round(us_cold, 3),
                     "gbps_algorithmic_cold": round(gbps_cold, 1),

@@ -183,7 +183,7 @@ int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hidden, i
                    void *const *shards_out, void *stream);
 
 /* The parity the next served call will use (0 or 1), or HG_EINVAL. With
- * device-side parity on, this synchronises the device and reads the word. */
+ * device-side parity on, this synchronises the device and reads it back. */
 int hg_parity(const hg_ctx *h);
 
 /*
@@ -191,9 +191,10 @@ int hg_parity(const hg_ctx *h);
  * default). Host-side parity cannot alternate when launches are replayed
  * from a graph, which is why calls under graph capture are otherwise
  * declined (API page, HeadGather class description and HeadGather.__call__
- * source). With device-side parity each launch reads the parity word when it
- * starts and the launch that completes a call (fused gather, collect) flips
- * it when its last workgroup finishes, so calls captured into a graph --
+ * source). With device-side parity each launch reads the parity from device
+ * memory when it starts and the launch that completes a call (fused gather,
+ * collect) writes the other parity back as its workgroups finish, with no
+ * wait between workgroups, so calls captured into a graph --
  * hg_gather, hg_push/hg_push_ranks + hg_collect, hg_gemm_gather -- are
  * served and every replay alternates. Switching on copies the host parity to
  * the device (stream-ordered); switching off waits for `stream` and copies it

@@ -28,7 +28,8 @@ using hg::u32x4;
 namespace {
 
 constexpr unsigned long long kDefaultPollLimit = 1ull << 24;
-constexpr int kStatusBytes = 256;
+constexpr int kSlotsOffset = 256;
+constexpr int kStatusBytes = kSlotsOffset + 4 * hg::kParitySlots;
 
 thread_local char g_last_error[256] = "";
 
@@ -98,7 +99,7 @@ struct hg_ctx {
   int cus = 0;
   long long vv = 0;             // 16-byte vectors per mailbox / output row
   u32x4 *box = nullptr;         // [2][cap][vv]
-  unsigned *status = nullptr;   // [0] poll timeouts, [1] finished workgroups, [2] parity word
+  unsigned *status = nullptr;   // [0] poll timeouts; parity slots from byte kSlotsOffset on
   bool dev_parity = false;      // parity kept in device memory (graph-capturable calls)
   int parity = 0;
   int pending_m = -1;           // split push awaiting its collect
@@ -110,16 +111,14 @@ struct hg_ctx {
   int fused_per_cu[4][4][3];
 
   u32x4 *parity_box(int p) const { return box + static_cast<long long>(p) * cap * vv; }
-  int *parity_word() const { return reinterpret_cast<int *>(status + 2); }
-  unsigned *done_word() const { return status + 1; }
+  int *parity_slots() const { return reinterpret_cast<int *>(status + kSlotsOffset / 4); }
   // Parity selection of a launch: host parity `p` in host mode, the device
   // word in device mode; `flip` on the launch that completes a call.
   hg::ParityArg parity_arg(int p, bool flip) const {
     hg::ParityArg pa;
     pa.box = box;
     pa.stride = static_cast<long long>(cap) * vv;
-    pa.dev = dev_parity ? parity_word() : nullptr;
-    pa.done = done_word();
+    pa.dev = dev_parity ? parity_slots() : nullptr;
     pa.p = p;
     pa.flip = flip ? 1 : 0;
     return pa;
@@ -193,7 +192,8 @@ int load_shards(int tp, int shard, const void *const *shards, int m, unsigned lo
 int split_grid(const hg_ctx *h, const Geometry &g, int block) {
   const int waves = block / 64;
   const long long tiles = (static_cast<long long>(g.chunks) + waves - 1) / waves;
-  const long long cap = static_cast<long long>(h->cus) * 16;
+  long long cap = static_cast<long long>(h->cus) * 16;
+  if (cap > hg::kParitySlots) cap = hg::kParitySlots;
   return static_cast<int>(tiles < cap ? tiles : cap);
 }
 
@@ -315,8 +315,8 @@ HG_API int hg_arm(hg_ctx *h, void *stream) {
   const int block = 256;
   long long grid = (vectors + block - 1) / block;
   if (grid > static_cast<long long>(h->cus) * 8) grid = static_cast<long long>(h->cus) * 8;
-  HIP_TRY(hg::launch_arm(h->box, vectors, h->parity_word(), h->done_word(), static_cast<int>(grid),
-                         block, static_cast<hipStream_t>(stream)));
+  HIP_TRY(hg::launch_arm(h->box, vectors, h->parity_slots(), static_cast<int>(grid), block,
+                         static_cast<hipStream_t>(stream)));
   h->parity = 0;
   h->pending_m = -1;
   h->pending_ranks = 0;
@@ -339,6 +339,7 @@ HG_API int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, voi
   const long long want = h->tune.fused_grid > 0 ? h->tune.fused_grid
                                                 : static_cast<long long>(kGridPerCu) * h->cus;
   if (want < lim) lim = want;
+  if (lim > hg::kParitySlots) lim = hg::kParitySlots;
   if (lim < 1) return HG_EINVAL;
   const int grid = static_cast<int>(tiles < lim ? tiles : lim);
   HIP_TRY(hg::launch_fused(table, g, md, h->parity_arg(h->parity, true), used_box_bytes(h, m),
@@ -503,7 +504,7 @@ HG_API int hg_parity(const hg_ctx *h) {
   if (!h->dev_parity) return h->parity;
   int v = -1;
   HIP_TRY(hipDeviceSynchronize());
-  HIP_TRY(hipMemcpy(&v, h->parity_word(), sizeof v, hipMemcpyDeviceToHost));
+  HIP_TRY(hipMemcpy(&v, h->parity_slots(), sizeof v, hipMemcpyDeviceToHost));
   return v;
 }
 
@@ -517,12 +518,11 @@ HG_API int hg_set_device_parity(hg_ctx *h, int enable, void *stream) {
   int rc = check_device(h);
   if (rc != HG_OK) return rc;
   if (enable && !h->dev_parity) {
-    HIP_TRY(hg::launch_set_word(h->parity_word(), h->parity, s));
-    HIP_TRY(hg::launch_set_word(reinterpret_cast<int *>(h->done_word()), 0, s));
+    HIP_TRY(hg::launch_set_slots(h->parity_slots(), h->parity, s));
     h->dev_parity = true;
   } else if (!enable && h->dev_parity) {
     int v = 0;
-    HIP_TRY(hipMemcpyAsync(&v, h->parity_word(), sizeof v, hipMemcpyDeviceToHost, s));
+    HIP_TRY(hipMemcpyAsync(&v, h->parity_slots(), sizeof v, hipMemcpyDeviceToHost, s));
     HIP_TRY(hipStreamSynchronize(s));
     h->parity = v & 1;
     h->dev_parity = false;

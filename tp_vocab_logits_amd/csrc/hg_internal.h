@@ -69,16 +69,24 @@ struct Modes {
   int rearm_stream;  // re-arm with non-temporal stores (1) or plain stores (0)
 };
 
+// Device-mode parity slots. All slots hold the same parity between launches.
+// Workgroup b of a launch reads slot b (mod the slot count). A launch that
+// completes a call (its grid is at most kParitySlots, one-dimensional) writes
+// the other parity into every slot s from workgroup s mod G, after all of
+// workgroup b's waves have used what they read from slot b; so no slot is
+// rewritten while a workgroup of that launch may still read it, and no
+// workgroup waits on another.
+constexpr int kParitySlots = 4096;
+
 // Which mailbox parity a launch uses. Host mode (`dev` null): parity `p`,
-// chosen by the host. Device mode: the launch reads the parity from *dev when
-// it starts and, if `flip`, the last of its workgroups to finish writes the
-// other parity back (finished workgroups are counted in *done). Device mode
-// keeps the alternation right when launches are replayed from a graph.
+// chosen by the host. Device mode: the launch reads the parity from the slots
+// when it starts and, if `flip`, writes the other parity back at its end.
+// Device mode keeps the alternation right when launches are replayed from a
+// graph.
 struct ParityArg {
   u32x4 *box;        // row 0 of parity 0; parity p starts at box + p * stride
   long long stride;  // 16-byte vectors per parity
-  int *dev;          // device parity word, or null
-  unsigned *done;    // finished-workgroup counter (device mode)
+  int *dev;          // kParitySlots device parity slots, or null
   int p;             // host-mode parity
   int flip;          // this launch completes a call (fused gather, collect)
 };
@@ -86,8 +94,9 @@ struct ParityArg {
 // Parity of a launch (device code).
 __device__ __forceinline__ int launch_parity(const ParityArg &pa) {
   if (!pa.dev) return pa.p;
-  return __builtin_amdgcn_readfirstlane(
-      __hip_atomic_load(pa.dev, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  const unsigned b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
+  return __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+      pa.dev + b % kParitySlots, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Builds the geometry for m rows at `vpt` vectors per lane.
@@ -96,11 +105,12 @@ Geometry make_geometry(int tp, int shard, int m, int vpt);
 // Kernel launchers. Each returns the launch status (hipGetLastError).
 // `box_bytes` is the size of the mailbox rows in use from `box` on (it bounds
 // the 128-bit coherent accesses, which use 32-bit offsets).
-// launch_arm also zeroes *pdev and *done when they are non-null.
-hipError_t launch_arm(u32x4 *box, long long vectors, int *pdev, unsigned *done, int grid, int block,
+// launch_arm also zeroes the kParitySlots parity slots at `slots` when
+// non-null.
+hipError_t launch_arm(u32x4 *box, long long vectors, int *slots, int grid, int block,
                       hipStream_t s);
-// *word := value (one thread).
-hipError_t launch_set_word(int *word, int value, hipStream_t s);
+// Every one of the kParitySlots parity slots := value.
+hipError_t launch_set_slots(int *slots, int value, hipStream_t s);
 hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md,
                         const ParityArg &pa, unsigned box_bytes, u32x4 *out, unsigned *status,
                         unsigned long long limit, int skew, int grid, int block, hipStream_t s);

@@ -175,6 +175,37 @@ __device__ __forceinline__ void push_chunk(const Table &sh, const Geometry &g, i
   }
 }
 
+// One chunk's push in two halves, for a caller that has not resolved the
+// destination yet: load_chunk issues the loads, store_chunk rewrites and
+// stores what they returned. Lanes past a ragged segment end load nothing.
+template <int VPT>
+struct LoadedChunk {
+  u32x4 v[VPT];
+  long long d;  // mailbox vector index of lane's first vector
+  int left;     // vectors of the segment from this lane on
+};
+
+template <int VPT, class Table>
+__device__ __forceinline__ LoadedChunk<VPT> load_chunk(const Table &sh, const Geometry &g, int c,
+                                                       int lane) {
+  const ChunkPos p = chunk_pos(c, g, VPT);
+  const u32x4 *src = sh.p[p.rank] + static_cast<long long>(p.row) * g.sv + p.k0 + lane;
+  LoadedChunk<VPT> L;
+  L.d = p.base + p.k0 + lane;
+  L.left = g.sv - p.k0 - lane;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+    L.v[i] = i * kWave < L.left ? load_stream(src + i * kWave) : u32x4{0u, 0u, 0u, 0u};
+  return L;
+}
+
+template <int VPT, int STORE>
+__device__ __forceinline__ void store_chunk(const LoadedChunk<VPT> &L, const Box &dst) {
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+    if (i * kWave < L.left) box_store<STORE>(dst, L.d + i * kWave, rewrite_sentinel(L.v[i]));
+}
+
 // Per-lane poll budget: re-reads left before the lane gives up.
 struct PollBudget {
   unsigned long long spins;
@@ -242,21 +273,45 @@ __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane
   }
 }
 
-// Device mode, completing launch: the last workgroup to finish flips the
-// parity word for the next launch on the stream. Every workgroup read the
-// parity before it counts itself here.
-__device__ __forceinline__ void finish_parity(const ParityArg &pa, int p) {
-  if (!pa.dev || !pa.flip) return;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned total = gridDim.x * gridDim.y * gridDim.z;
-    const unsigned old = __hip_atomic_fetch_add(pa.done, 1u, __ATOMIC_ACQ_REL,
-                                                __HIP_MEMORY_SCOPE_AGENT);
-    if (old == total - 1) {
-      __hip_atomic_store(pa.done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(pa.dev, p ^ 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+// A launch that completes a call (one-dimensional grid of at most
+// kParitySlots workgroups) hands the other parity to the next launch in device
+// mode, in two steps. take_parity reads the parity and, with a barrier, makes
+// sure every wave of workgroup b holds the value it read from slot b.
+// pass_parity, at the launch's end, writes the other parity into slots b,
+// b + G, b + 2G, ... No other workgroup of this launch reads those slots, and
+// the next launch on the stream, their only other reader, starts after this
+// one has ended, so relaxed stores suffice and nothing waits on them. The
+// value to store and the lane's first slot address are put in vector
+// registers at the start, so the final stores need not wait for earlier
+// stores to release the registers holding their data.
+struct NextParity {
+  int p;      // this launch's parity
+  int next;   // p ^ 1, held in a vector register
+  int *slot;  // this lane's first slot, held in vector registers
+};
+
+__device__ __forceinline__ NextParity take_parity(const ParityArg &pa) {
+  NextParity np;
+  np.p = launch_parity(pa);
+  np.next = 0;
+  np.slot = pa.dev + blockIdx.x + threadIdx.x * gridDim.x;
+  if (pa.dev && pa.flip) {
+    __asm__ __volatile__("v_mov_b32 %0, %1" : "=v"(np.next) : "s"(np.p ^ 1) : "memory");
+    __asm__ __volatile__("" : "+v"(np.slot));
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
   }
+  return np;
+}
+
+__device__ __forceinline__ void pass_parity(const ParityArg &pa, const NextParity &np) {
+  if (!pa.dev || !pa.flip || threadIdx.x >= kWave) return;
+  const int grid = static_cast<int>(gridDim.x);
+  // global address space, so the stores stay global rather than flat
+  auto *q = (__attribute__((address_space(1))) int *)np.slot;
+  for (int s = static_cast<int>(blockIdx.x + threadIdx.x * gridDim.x); s < kParitySlots;
+       s += kWave * grid, q += kWave * grid)
+    __hip_atomic_store(q, np.next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ int wave_id() {
@@ -271,14 +326,13 @@ __device__ __forceinline__ int waves_per_block() { return static_cast<int>(block
 // Kernels
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(1024) void k_arm(u32x4 *box, long long vectors, int *pdev,
-                                              unsigned *done) {
+__global__ __launch_bounds__(1024) void k_arm(u32x4 *box, long long vectors, int *slots) {
   const u32x4 armed = {kSentinel, kSentinel, kSentinel, kSentinel};
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    if (pdev) *pdev = 0;
-    if (done) *done = 0u;
-  }
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+  if (slots)
+    for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+         i < kParitySlots; i += stride)
+      slots[i] = 0;
   for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < vectors;
        i += stride)
     box[i] = armed;
@@ -298,17 +352,24 @@ __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, 
                                                 unsigned box_bytes, u32x4 *out, unsigned *status,
                                                 unsigned long long limit, int skew,
                                                 int rearm_stream) {
-  const int p = launch_parity(pa);
-  u32x4 *box_ptr = pa.box + p * pa.stride;
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
   const int tiles = (g.chunks + waves - 1) / waves;
   const int grid = static_cast<int>(gridDim.x);
   const int me = static_cast<int>(blockIdx.x);
-  const Box box = make_box(box_ptr, box_bytes);
 
-  for (int t = me; t < tiles; t += grid) {
+  // The first chunk's loads go out before the parity is read, so that in
+  // device mode the two memory latencies overlap.
+  const int c0 = me * waves + wave;
+  const bool first = me < tiles && c0 < g.chunks;
+  LoadedChunk<VPT> L0;
+  if (first) L0 = load_chunk<VPT>(sh, g, c0, lane);
+  const NextParity np = take_parity(pa);
+  const Box box = make_box(pa.box + np.p * pa.stride, box_bytes);
+  if (first) store_chunk<VPT, PUSH>(L0, box);
+
+  for (int t = me + grid; t < tiles; t += grid) {
     const int c = t * waves + wave;
     if (c < g.chunks) push_chunk<VPT, true, PUSH>(sh, g, c, lane, box);
   }
@@ -321,7 +382,7 @@ __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, 
     const int c = t * waves + wave;
     if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud, rearm_stream);
   }
-  finish_parity(pa, p);
+  pass_parity(pa, np);
 }
 
 // Split variant, first half: the push alone, by the ranks whose bit is set in
@@ -348,8 +409,8 @@ template <int VPT, int POLL>
 __global__ __launch_bounds__(1024) void k_collect(Geometry g, ParityArg pa, unsigned box_bytes,
                                                   u32x4 *out, unsigned *status,
                                                   unsigned long long limit, int rearm_stream) {
-  const int p = launch_parity(pa);
-  u32x4 *box_ptr = pa.box + p * pa.stride;
+  const NextParity np = take_parity(pa);
+  u32x4 *box_ptr = pa.box + np.p * pa.stride;
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
@@ -360,10 +421,14 @@ __global__ __launch_bounds__(1024) void k_collect(Geometry g, ParityArg pa, unsi
     const int c = t * waves + wave;
     if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud, rearm_stream);
   }
-  finish_parity(pa, p);
+  pass_parity(pa, np);
 }
 
-__global__ void k_set_word(int *word, int value) { *word = value; }
+__global__ __launch_bounds__(256) void k_set_slots(int *slots, int value) {
+  for (int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x); i < kParitySlots;
+       i += static_cast<int>(gridDim.x * blockDim.x))
+    slots[i] = value;
+}
 
 // The stock path's single-device share: rank-order concatenation, bytes
 // unchanged.
@@ -440,14 +505,14 @@ Geometry make_geometry(int tp, int shard, int m, int vpt) {
   return g;
 }
 
-hipError_t launch_arm(u32x4 *box, long long vectors, int *pdev, unsigned *done, int grid, int block,
+hipError_t launch_arm(u32x4 *box, long long vectors, int *slots, int grid, int block,
                       hipStream_t s) {
-  hipLaunchKernelGGL(k_arm, dim3(grid), dim3(block), 0, s, box, vectors, pdev, done);
+  hipLaunchKernelGGL(k_arm, dim3(grid), dim3(block), 0, s, box, vectors, slots);
   return hipGetLastError();
 }
 
-hipError_t launch_set_word(int *word, int value, hipStream_t s) {
-  hipLaunchKernelGGL(k_set_word, dim3(1), dim3(1), 0, s, word, value);
+hipError_t launch_set_slots(int *slots, int value, hipStream_t s) {
+  hipLaunchKernelGGL(k_set_slots, dim3(kParitySlots / 256), dim3(256), 0, s, slots, value);
   return hipGetLastError();
 }
 
