@@ -93,14 +93,18 @@ int hg_arm(hg_ctx *h, void *stream);
  * shards: host array of tp device pointers; shards[r] is rank r's [m][shard]
  *         BF16 block, row-major, contiguous (row stride = shard elements).
  * m:      rows to gather this call.
- * out:    device [m][tp*shard] BF16, row-major; receives rank r's row i at
- *         columns r*shard .. r*shard+shard-1 of row i, every sentinel word
- *         rewritten to zero. Must not overlap the shards or the mailbox.
+ * out:    device [m][vocab] BF16, row-major, 16-byte aligned (vocab =
+ *         tp*shard unless hg_set_vocab chose fewer columns); gathered row i,
+ *         which holds rank r's row i at columns r*shard .. r*shard+shard-1
+ *         with every sentinel word rewritten to zero, is written to row i of
+ *         `out` up to column vocab-1. Must not overlap the shards or the
+ *         mailbox.
  *
  * HG_EDECLINE (stock path, parity unchanged) when m == 0, m > cap, or the
- * stream is capturing a graph (host-side parity cannot alternate under
- * replay). HG_EINVAL for m < 0, NULL / misaligned / overlapping pointers.
- * HG_ESTATE if a split push is pending. On HG_OK the parity flips.
+ * stream is capturing a graph while the parity is kept on the host (it cannot
+ * alternate under replay; see hg_set_device_parity). HG_EINVAL for m < 0,
+ * NULL / misaligned / overlapping pointers. HG_ESTATE if a split push is
+ * pending. On HG_OK the parity flips.
  */
 int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, void *stream);
 
@@ -128,10 +132,10 @@ int hg_push_ranks(hg_ctx *h, const void *const *shards, int m, unsigned long lon
 
 /*
  * Split variant, second half: poll rows 0..m-1 of the pending parity until no
- * word is the sentinel, copy them to `out` ([m][tp*shard] BF16) and re-arm
- * them; then flip the parity. HG_ESTATE unless a push of the same m is
- * pending (from any set of ranks); HG_EDECLINE (nothing changes) if the
- * stream is capturing.
+ * word is the sentinel, copy them to `out` ([m][vocab] BF16, as for
+ * hg_gather) and re-arm them; then flip the parity. HG_ESTATE unless a push
+ * of the same m is pending (from any set of ranks); HG_EDECLINE (nothing
+ * changes) if the stream is capturing while the parity is kept on the host.
  */
 int hg_collect(hg_ctx *h, int m, void *out, void *stream);
 
@@ -201,6 +205,21 @@ int hg_parity(const hg_ctx *h);
  * back. HG_ESTATE while a split push is pending; HG_EINVAL while capturing.
  */
 int hg_set_device_parity(hg_ctx *h, int enable, void *stream);
+
+/*
+ * The padded-vocab slice, folded into the copy step (PR page, Purpose: the
+ * gathered logits keep only the real vocabulary's columns after the gather).
+ * From the next served call on, hg_gather, hg_collect and hg_gemm_gather
+ * write `out` as [m][vocab]: the first `vocab` columns of each gathered row.
+ * The mailbox protocol is unchanged -- every word is pushed, polled and
+ * re-armed. vocab = tp*shard (the default) writes whole rows; vocab % 8 == 0
+ * keeps 16-byte stores, other widths store element by element. HG_EINVAL
+ * unless 1 <= vocab <= tp*shard. Calls already enqueued keep their width.
+ */
+int hg_set_vocab(hg_ctx *h, int vocab);
+
+/* Output columns per row of served calls (see hg_set_vocab), or HG_EINVAL. */
+int hg_vocab(const hg_ctx *h);
 
 /* Read-only view of one parity of the mailbox, for inspection by tests:
  * *dev = device address of [cap][tp*shard] BF16, *bytes = its size. */

@@ -112,6 +112,17 @@ def gather_definition(shards) -> np.ndarray:
     return unpack_words(rewrite_sentinel(pack_words(stock_concat(shards))))
 
 
+def slice_vocab(out, vocab: int) -> np.ndarray:
+    """The padded-vocab slice taken after the gather (PR page, Purpose: the
+    gather keeps its semantics, the slice to the real vocabulary included):
+    the first ``vocab`` columns of every gathered row, as a new ``[M, vocab]``
+    array. ``1 <= vocab <= V``."""
+    out = np.asarray(out, dtype=np.uint16)
+    if not 1 <= vocab <= out.shape[1]:
+        raise ValueError(f"vocab {vocab} outside 1..{out.shape[1]}")
+    return out[:, :vocab].copy()
+
+
 # ---------------------------------------------------------------------------
 # Construction rules
 # ---------------------------------------------------------------------------

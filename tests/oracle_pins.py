@@ -278,9 +278,31 @@ def check_create_rules(g) -> None:
     assert g.create_ok(8, 20480, 256)
 
 
+def check_vocab_slice(g) -> None:
+    """The padded-vocab slice against the hand-worked golden output: its first
+    columns in order, nothing reordered, the full width an exact copy."""
+    gd = read_golden("gather_tp2_s8_m2.txt")
+    tp, shard, m = int(gd["tp"][0][0]), int(gd["width"][0][0]), int(gd["rows"][0][0])
+    want = np.zeros((m, tp * shard), np.uint16)
+    for row, *vals in gd["out"]:
+        want[int(row)] = [int(v, 16) for v in vals]
+    for vocab in (1, 3, 8, 9, 15, tp * shard):
+        got = g.slice_vocab(want, vocab)
+        assert got.shape == (m, vocab)
+        for i in range(m):
+            for j in range(vocab):
+                assert got[i, j] == want[i, j], (vocab, i, j)
+    for bad in (0, tp * shard + 1):
+        try:
+            g.slice_vocab(want, bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"vocab {bad} accepted")
+
+
 GATHER_CHECKS = [check_sentinel_constant, check_packing, check_golden_gather, check_layout_nccl,
                  check_value_equivalence_and_xor, check_exhaustive_tiny, check_protocol,
-                 check_partial_push, check_create_rules]
+                 check_partial_push, check_create_rules, check_vocab_slice]
 
 
 # ---------------------------------------------------------------------------

@@ -74,6 +74,9 @@ def test_null_context_paths():
     v = ctypes.c_int()
     assert lib.hg_get_tuning(null, _lib.TUNE_FUSED_BLOCK, ctypes.byref(v)) == _lib.HG_EINVAL
     assert lib.hg_fused_grid_limit(null, 1) == _lib.HG_EINVAL
+    assert lib.hg_set_device_parity(null, 1, None) == _lib.HG_EINVAL
+    assert lib.hg_set_vocab(null, 5) == _lib.HG_EINVAL
+    assert lib.hg_vocab(null) == _lib.HG_EINVAL
 
 
 def test_stock_gather_argument_checks():

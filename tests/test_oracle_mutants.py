@@ -167,7 +167,23 @@ def _bf16_to_f64_wrong_shift(bits):
     return (b.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
 
 
+def _slice_tail(out, vocab):
+    out = np.asarray(out, np.uint16)
+    return out[:, out.shape[1] - vocab:].copy()
+
+
+def _slice_one_short(out, vocab):
+    out = np.asarray(out, np.uint16)
+    if not 1 <= vocab <= out.shape[1]:
+        raise ValueError("vocab")
+    keep = out[:, :vocab].copy()
+    keep[:, -1] = 0
+    return keep
+
+
 MUTANTS = [
+    ("vocab slice keeps the last columns", gather, {"slice_vocab": _slice_tail}),
+    ("vocab slice drops its last column", gather, {"slice_vocab": _slice_one_short}),
     ("pack high/low swapped", gather, {"pack_words": _pack_swapped, "unpack_words": _unpack_swapped}),
     ("sentinel constant (-0,+0)", gather, {"SENT_WORD": 0x00008000}),
     ("rewrites any word with -0 high half", gather, {"rewrite_sentinel": _rewrite_any_neg_zero_high}),

@@ -55,6 +55,8 @@ SIGNATURES = {
     "hg_gemm_gather": (_i, [_ctxp, _vp, ctypes.POINTER(_vp), _i, _i, _vp, ctypes.POINTER(_vp), _vp]),
     "hg_parity": (_i, [_ctxp]),
     "hg_set_device_parity": (_i, [_ctxp, _i, _vp]),
+    "hg_set_vocab": (_i, [_ctxp, _i]),
+    "hg_vocab": (_i, [_ctxp]),
     "hg_mailbox": (_i, [_ctxp, _i, ctypes.POINTER(_vp), ctypes.POINTER(_size)]),
     "hg_copy_mailbox": (_i, [_ctxp, _i, _vp, _vp]),
     "hg_set_poll_limit": (_i, [_ctxp, _ull]),

@@ -97,7 +97,8 @@ struct hg_ctx {
   int tp = 0, shard = 0, cap = 0;
   int device = -1;
   int cus = 0;
-  long long vv = 0;             // 16-byte vectors per mailbox / output row
+  long long vv = 0;             // 16-byte vectors per mailbox row
+  int vocab = 0;                // BF16 columns per output row (padded-vocab slice), 1..tp*shard
   u32x4 *box = nullptr;         // [2][cap][vv]
   unsigned *status = nullptr;   // [0] poll timeouts; parity slots from byte kSlotsOffset on
   bool dev_parity = false;      // parity kept in device memory (graph-capturable calls)
@@ -124,6 +125,14 @@ struct hg_ctx {
     return pa;
   }
   size_t row_bytes() const { return static_cast<size_t>(vv) * 16; }
+  size_t out_row_bytes() const { return static_cast<size_t>(vocab) * 2; }
+  hg::OutRows out_rows(void *out) const {
+    hg::OutRows o;
+    o.ptr = static_cast<u32x4 *>(out);
+    o.cols = vocab;
+    o.cvec = vocab % 8 == 0 ? vocab / 8 : 0;
+    return o;
+  }
 };
 
 namespace {
@@ -237,7 +246,7 @@ int check_call(hg_ctx *h, const void *const *shards, int m, unsigned long long r
   if (cs == HG_EDECLINE && !h->dev_parity) return HG_EDECLINE;  // host parity cannot be replayed
   int rc = check_device(h);
   if (rc != HG_OK) return rc;
-  const size_t out_bytes = static_cast<size_t>(m) * h->row_bytes();
+  const size_t out_bytes = static_cast<size_t>(m) * h->out_row_bytes();
   const size_t box_bytes = static_cast<size_t>(2) * h->cap * h->row_bytes();
   if (out) {
     if (!aligned16(out) || overlaps(out, out_bytes, h->box, box_bytes)) return HG_EINVAL;
@@ -261,6 +270,7 @@ HG_API int hg_create(int tp, int shard, int cap, hg_ctx **out) {
   h->shard = shard;
   h->cap = cap;
   h->vv = vv;
+  h->vocab = tp * shard;
   auto fail = [&](int rc) {
     if (h->box) (void)hipFree(h->box);
     if (h->status) (void)hipFree(h->status);
@@ -343,7 +353,7 @@ HG_API int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, voi
   if (lim < 1) return HG_EINVAL;
   const int grid = static_cast<int>(tiles < lim ? tiles : lim);
   HIP_TRY(hg::launch_fused(table, g, md, h->parity_arg(h->parity, true), used_box_bytes(h, m),
-                           static_cast<u32x4 *>(out), h->status, h->poll_limit, h->tune.poll_skew,
+                           h->out_rows(out), h->status, h->poll_limit, h->tune.poll_skew,
                            grid, h->tune.fused_block, static_cast<hipStream_t>(stream)));
   if (!h->dev_parity) h->parity ^= 1;
   return HG_OK;
@@ -380,14 +390,14 @@ HG_API int hg_collect(hg_ctx *h, int m, void *out, void *stream) {
   if (cs == HG_EDECLINE && !h->dev_parity) return HG_EDECLINE;
   int rc = check_device(h);
   if (rc != HG_OK) return rc;
-  const size_t out_bytes = static_cast<size_t>(m) * h->row_bytes();
+  const size_t out_bytes = static_cast<size_t>(m) * h->out_row_bytes();
   const size_t box_bytes = static_cast<size_t>(2) * h->cap * h->row_bytes();
   if (!out || !aligned16(out) || overlaps(out, out_bytes, h->box, box_bytes)) return HG_EINVAL;
   const hg::Modes md = pick_modes(h, h->tune.split_vpt, m);
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
   const int block = h->tune.split_block;
   HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->pending_parity, true), used_box_bytes(h, m),
-                             static_cast<u32x4 *>(out), h->status, h->poll_limit,
+                             h->out_rows(out), h->status, h->poll_limit,
                              split_grid(h, g, block), block, static_cast<hipStream_t>(stream)));
   h->pending_m = -1;
   h->pending_ranks = 0;
@@ -480,7 +490,7 @@ HG_API int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hi
   hg::OutTable ot;
   rc = check_lmhead(h->tp, h->shard, x, w, hidden, m, shards_out, &wt, &ot);
   if (rc != HG_OK) return rc;
-  const size_t out_bytes = static_cast<size_t>(m) * h->row_bytes();
+  const size_t out_bytes = static_cast<size_t>(m) * h->out_row_bytes();
   const size_t box_bytes = static_cast<size_t>(2) * h->cap * h->row_bytes();
   if (!out || !aligned16(out) || overlaps(out, out_bytes, h->box, box_bytes) ||
       overlaps(out, out_bytes, x, static_cast<size_t>(m) * hidden * 2))
@@ -493,7 +503,7 @@ HG_API int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hi
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
   const int block = h->tune.split_block;
   HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->parity, true), used_box_bytes(h, m),
-                             static_cast<u32x4 *>(out), h->status, h->poll_limit,
+                             h->out_rows(out), h->status, h->poll_limit,
                              split_grid(h, g, block), block, s));
   if (!h->dev_parity) h->parity ^= 1;
   return HG_OK;
@@ -529,6 +539,14 @@ HG_API int hg_set_device_parity(hg_ctx *h, int enable, void *stream) {
   }
   return HG_OK;
 }
+
+HG_API int hg_set_vocab(hg_ctx *h, int vocab) {
+  if (!h || vocab < 1 || vocab > h->tp * h->shard) return HG_EINVAL;
+  h->vocab = vocab;
+  return HG_OK;
+}
+
+HG_API int hg_vocab(const hg_ctx *h) { return h ? h->vocab : HG_EINVAL; }
 
 HG_API int hg_mailbox(const hg_ctx *h, int parity, const void **dev, size_t *bytes) {
   if (!h || (parity != 0 && parity != 1) || !dev || !bytes) return HG_EINVAL;

@@ -69,6 +69,17 @@ struct Modes {
   int rearm_stream;  // re-arm with non-temporal stores (1) or plain stores (0)
 };
 
+// Where the copy step writes. Row i of the gathered logits goes to
+// out + i * cols BF16 elements, and only its columns 0 .. cols-1 are written
+// (the padded-vocab slice; cols = tp * shard is the whole row). With
+// cols % 8 == 0 the rows are 16-byte aligned and take whole-vector stores
+// (cvec = cols / 8); otherwise cvec = 0 and the copy stores element by element.
+struct OutRows {
+  u32x4 *ptr;
+  int cols;
+  int cvec;
+};
+
 // Device-mode parity slots. All slots hold the same parity between launches.
 // Workgroup b of a launch reads slot b (mod the slot count). A launch that
 // completes a call (its grid is at most kParitySlots, one-dimensional) writes
@@ -112,12 +123,12 @@ hipError_t launch_arm(u32x4 *box, long long vectors, int *slots, int grid, int b
 // Every one of the kParitySlots parity slots := value.
 hipError_t launch_set_slots(int *slots, int value, hipStream_t s);
 hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md,
-                        const ParityArg &pa, unsigned box_bytes, u32x4 *out, unsigned *status,
+                        const ParityArg &pa, unsigned box_bytes, const OutRows &out, unsigned *status,
                         unsigned long long limit, int skew, int grid, int block, hipStream_t s);
 hipError_t launch_push(const ShardTable &sh, const Geometry &g, int vpt, const ParityArg &pa,
                        unsigned long long ranks, int grid, int block, hipStream_t s);
 hipError_t launch_collect(const Geometry &g, const Modes &md, const ParityArg &pa,
-                          unsigned box_bytes, u32x4 *out, unsigned *status,
+                          unsigned box_bytes, const OutRows &out, unsigned *status,
                           unsigned long long limit, int grid, int block, hipStream_t s);
 hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *out, int grid,
                         int block, hipStream_t s);

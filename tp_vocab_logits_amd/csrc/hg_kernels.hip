@@ -239,15 +239,31 @@ __device__ __forceinline__ void rearm_store(const Box &b, long long idx, bool st
     b.ptr[idx] = armed;
 }
 
+// Copy one polled vector (BF16 columns 8*cv .. 8*cv+7 of gathered row `row`)
+// to the output, keeping only the columns below o.cols.
+__device__ __forceinline__ void out_store(const OutRows &o, int row, int cv, u32x4 v) {
+  if (o.cvec) {
+    if (cv < o.cvec) store_stream(o.ptr + static_cast<long long>(row) * o.cvec + cv, v);
+    return;
+  }
+  const int left = o.cols - cv * 8;  // columns of the row from this vector on
+  if (left <= 0) return;
+  unsigned short *e = reinterpret_cast<unsigned short *>(o.ptr) +
+                      static_cast<long long>(row) * o.cols + static_cast<long long>(cv) * 8;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < left) e[j] = static_cast<unsigned short>(v[j >> 1] >> (16 * (j & 1)));
+}
+
 // Poll one chunk of the mailbox until no word is the sentinel, copy it to
-// `out` and re-arm it.
+// the output and re-arm it.
 template <int VPT, int POLL>
 __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane, const Box &box,
-                                              u32x4 *out, unsigned *status, PollBudget &bud,
-                                              bool rearm_stream) {
+                                              const OutRows &out, unsigned *status,
+                                              PollBudget &bud, bool rearm_stream) {
   const ChunkPos p = chunk_pos(c, g, VPT);
   const long long d = p.base + p.k0 + lane;
-  u32x4 *o = out + d;
+  const int cv = p.rank * g.sv + p.k0 + lane;  // column vector of the output row
   if (p.k0 + kWave * VPT <= g.sv) {
     u32x4 v[VPT];
 #pragma unroll
@@ -256,7 +272,7 @@ __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane
     for (int i = 0; i < VPT; ++i) v[i] = await_vec<POLL>(box, d + i * kWave, v[i], status, bud);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      store_stream(o + i * kWave, v[i]);
+      out_store(out, p.row, cv + i * kWave, v[i]);
       rearm_store(box, d + i * kWave, rearm_stream);
     }
   } else {
@@ -266,7 +282,7 @@ __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane
       if (i * kWave < left) {
         const long long idx = d + i * kWave;
         const u32x4 v = await_vec<POLL>(box, idx, box_load<POLL>(box, idx), status, bud);
-        store_stream(o + i * kWave, v);
+        out_store(out, p.row, cv + i * kWave, v);
         rearm_store(box, idx, rearm_stream);
       }
     }
@@ -349,7 +365,7 @@ __global__ __launch_bounds__(1024) void k_arm(u32x4 *box, long long vectors, int
 // wait is on a workgroup dispatched earlier.
 template <int VPT, int PUSH, int POLL, int NT>
 __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, ParityArg pa,
-                                                unsigned box_bytes, u32x4 *out, unsigned *status,
+                                                unsigned box_bytes, OutRows out, unsigned *status,
                                                 unsigned long long limit, int skew,
                                                 int rearm_stream) {
   const int waves = waves_per_block();
@@ -407,7 +423,7 @@ __global__ __launch_bounds__(1024) void k_push(ShardTableN<NT> sh, Geometry g, P
 // Split variant, second half: poll, copy, re-arm.
 template <int VPT, int POLL>
 __global__ __launch_bounds__(1024) void k_collect(Geometry g, ParityArg pa, unsigned box_bytes,
-                                                  u32x4 *out, unsigned *status,
+                                                  OutRows out, unsigned *status,
                                                   unsigned long long limit, int rearm_stream) {
   const NextParity np = take_parity(pa);
   u32x4 *box_ptr = pa.box + np.p * pa.stride;
@@ -517,7 +533,7 @@ hipError_t launch_set_slots(int *slots, int value, hipStream_t s) {
 }
 
 hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md,
-                        const ParityArg &pa, unsigned box_bytes, u32x4 *out, unsigned *status,
+                        const ParityArg &pa, unsigned box_bytes, const OutRows &out, unsigned *status,
                         unsigned long long limit, int skew, int grid, int block, hipStream_t s) {
   return by_table(sh, g.tp, [&](const auto &t) {
     constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
@@ -547,7 +563,7 @@ hipError_t launch_push(const ShardTable &sh, const Geometry &g, int vpt, const P
 }
 
 hipError_t launch_collect(const Geometry &g, const Modes &md, const ParityArg &pa,
-                          unsigned box_bytes, u32x4 *out, unsigned *status,
+                          unsigned box_bytes, const OutRows &out, unsigned *status,
                           unsigned long long limit, int grid, int block, hipStream_t s) {
   return by_vpt(md.vpt, [&](auto v) {
     return by_poll(md.poll, [&](auto po) {

@@ -114,9 +114,14 @@ def lmhead(x: torch.Tensor, w, tp: int, shard: int,
 
 class HeadGather:
     """One gather context: ``tp`` virtual ranks of ``shard`` BF16 columns, up to
-    ``cap`` rows per call, on ``device`` (default: the current CUDA device)."""
+    ``cap`` rows per call, on ``device`` (default: the current CUDA device).
+    ``vocab`` (default ``tp * shard``) is the real vocabulary: outputs are
+    ``[M, vocab]``, the padded-vocab slice of each gathered row, taken inside
+    the copy step (``hg_set_vocab``); declined calls return the same slice of
+    the stock gather."""
 
-    def __init__(self, tp: int, shard: int, cap: int, device: torch.device | int | None = None):
+    def __init__(self, tp: int, shard: int, cap: int, device: torch.device | int | None = None,
+                 vocab: int | None = None):
         if device is None:
             index = torch.cuda.current_device()
         elif isinstance(device, int):
@@ -126,10 +131,18 @@ class HeadGather:
             index = d.index if d.index is not None else torch.cuda.current_device()
         self.device = torch.device("cuda", index)
         self.tp, self.shard, self.cap = int(tp), int(shard), int(cap)
-        self.vocab = self.tp * self.shard
+        self.width = self.tp * self.shard  # V, the padded vocabulary
         self._h = ctypes.c_void_p()
         with torch.cuda.device(self.device):
             check(lib().hg_create(self.tp, self.shard, self.cap, ctypes.byref(self._h)), "hg_create")
+        self.vocab = self.width
+        if vocab is not None:
+            self.set_vocab(vocab)
+
+    def set_vocab(self, vocab: int) -> None:
+        """Output columns per row from the next call on (1..V)."""
+        check(lib().hg_set_vocab(self._h, int(vocab)), "hg_set_vocab")
+        self.vocab = int(vocab)
 
     # -- lifetime ----------------------------------------------------------
     def close(self) -> None:
@@ -156,19 +169,31 @@ class HeadGather:
             raise ValueError(f"out must be a contiguous BF16 [{m}, {self.vocab}] tensor")
         return out
 
+    def _stock(self, shards, s: int, out: torch.Tensor | None) -> torch.Tensor:
+        """The stock gather; shards of this context's width are sliced to the
+        vocabulary like a served call."""
+        if self.vocab == self.width or s != self.shard:
+            return stock_gather(shards, self.tp, out)
+        full = stock_gather(shards, self.tp)
+        part = full[:, : self.vocab]
+        if out is None:
+            return part.contiguous()
+        out.copy_(part)
+        return out
+
     def __call__(self, shards, out: torch.Tensor | None = None) -> torch.Tensor:
-        """Gather ``[M, S]`` x TP -> ``[M, V]``. Served calls run the fused
+        """Gather ``[M, S]`` x TP -> ``[M, vocab]``. Served calls run the fused
         kernel and flip the parity; declined calls return the stock gather."""
         info = _shard_pointers(shards, self.tp)
         ptrs, m = info[0], info[1]
         if not self._eligible(info):
-            return stock_gather(shards, self.tp, out)
+            return self._stock(shards, info[2], out)
         out = self._out(m, out)
         with torch.cuda.device(self.device):
             rc = lib().hg_gather(self._h, pointer_array(ptrs), m, ctypes.c_void_p(out.data_ptr()),
                                  _stream_handle(self.device))
         if rc == HG_EDECLINE:
-            return stock_gather(shards, self.tp, out)
+            return self._stock(shards, info[2], out)
         check(rc, "hg_gather")
         return out
 
@@ -196,7 +221,7 @@ class HeadGather:
         return check(rc, "hg_push_ranks") == HG_OK
 
     def collect(self, m: int, out: torch.Tensor | None = None) -> torch.Tensor:
-        """Split variant, second half: the gathered ``[m, V]`` logits."""
+        """Split variant, second half: the gathered ``[m, vocab]`` logits."""
         out = self._out(m, out)
         with torch.cuda.device(self.device):
             rc = lib().hg_collect(self._h, m, ctypes.c_void_p(out.data_ptr()),
@@ -245,7 +270,7 @@ class HeadGather:
 
     def mailbox(self, parity: int) -> torch.Tensor:
         """A copy of one parity of the mailbox as ``[cap, V]`` BF16 (stream-ordered)."""
-        dst = torch.empty((self.cap, self.vocab), dtype=torch.bfloat16, device=self.device)
+        dst = torch.empty((self.cap, self.width), dtype=torch.bfloat16, device=self.device)
         with torch.cuda.device(self.device):
             check(lib().hg_copy_mailbox(self._h, parity, ctypes.c_void_p(dst.data_ptr()),
                                         _stream_handle(self.device)), "hg_copy_mailbox")
