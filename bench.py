@@ -15,8 +15,14 @@ its results double as the check of the GPU outputs; a mismatch aborts the run.
 Algorithmic bytes per gather: 5 * M * V * 2 (shard read, mailbox push write,
 mailbox poll read, output write, re-arm write).
 
+The JSON line also carries ``decode_graph``: the same K decode gathers
+captured into one HIP graph, with the parity kept in device memory, replayed
+and timed per gather.
+
 Modes: default (the JSON line); ``--pmc-probe`` runs only a plain 256 MiB copy
-and the M=256 fused gather a few times, for ``rocprofv3 --pmc`` counter runs.
+and the M=256 fused gather a few times, for ``rocprofv3 --pmc`` counter runs;
+``--graph-only`` runs only the graph-replay leg (checked against the oracle),
+for a kernel trace of it.
 """
 
 from __future__ import annotations
@@ -59,6 +65,8 @@ def parse_args():
     ap.add_argument("--pmc-probe", action="store_true")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the graph-replay leg of the M=1 decode gather")
+    ap.add_argument("--graph-only", action="store_true",
+                    help="run only the graph-replay leg (for a kernel trace of it), check it, exit")
     ap.add_argument("--producer-steps", type=int, default=10,
                     help="timed M=256 lm_head producer + gather calls (0: skip)")
     return ap.parse_args()
@@ -156,6 +164,45 @@ def main() -> int:
     out_ptrs = [ctypes.c_void_p(outs[n].data_ptr()) for n in range(n_out)]
     fn = call_fn(hg, args.variant)
 
+    # ---------------- decode, captured: the same K gathers replayed from a graph
+    # (parity kept in device memory so that every replay alternates it)
+    def graph_leg():
+        hg_g = HeadGather(wd.tp, wd.shard, wd.cap, device=dev)
+        hg_g.set_device_parity(True)
+        g_outs = torch.empty((n_out, wd.rows, wd.vocab), dtype=torch.bfloat16, device=dev)
+        g_ptrs = [ctypes.c_void_p(g_outs[n].data_ptr()) for n in range(n_out)]
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        rc = 0
+        with torch.cuda.graph(graph, stream=side):
+            gs = ctypes.c_void_p(side.cuda_stream)
+            for n in range(args.steps):
+                rc |= lib.hg_gather(hg_g.handle, dec_ptrs[n % wd.pool], wd.rows, g_ptrs[n], gs)
+        if rc:
+            raise _lib.HgError(-abs(rc), "graph capture")
+        graph.replay()
+        torch.cuda.synchronize()
+        log(f"decode graph replay of {args.steps} captured gathers")
+        with Timer(torch, stream) as t_g:
+            graph.replay()
+        return t_g.ms * 1000.0 / args.steps, hg_g, g_outs
+
+    if args.graph_only:
+        from oracle import gather as og
+
+        us, hg_g, g_outs = graph_leg()
+        got = g_outs[: wd.pool].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        for k in range(min(wd.pool, args.steps)):
+            if not np.array_equal(got[k], og.gather_definition(list(dec_sets[k]))):
+                log(f"FAIL: graph-replayed decode output of call {k} differs from the oracle")
+                return 1
+        if hg_g.parity != 0 or hg_g.poll_status() != _lib.HG_OK:
+            log("FAIL: device parity or poll status after the graph replays")
+            return 1
+        log(f"graph-only: {us:.3f} us per captured M=1 gather; outputs match the oracle")
+        return 0
+
     log(f"decode warmup {args.warmup}")
     for n in range(args.warmup):
         rc = fn(dec_ptrs[n % wd.pool], wd.rows, out_ptrs[n % n_out])
@@ -170,29 +217,9 @@ def main() -> int:
         raise _lib.HgError(-abs(rcs), "timed decode loop")
     us_m1 = t_dec.ms * 1000.0 / args.steps
 
-    # ---------------- decode, captured: the same K gathers replayed from a graph
-    # (parity kept in device memory so that every replay alternates it)
     us_graph = None
     if args.variant == "fused" and args.graph:
-        hg_g = HeadGather(wd.tp, wd.shard, wd.cap, device=dev)
-        hg_g.set_device_parity(True)
-        g_outs = torch.empty((n_out, wd.rows, wd.vocab), dtype=torch.bfloat16, device=dev)
-        g_ptrs = [ctypes.c_void_p(g_outs[n].data_ptr()) for n in range(n_out)]
-        side = torch.cuda.Stream(device=dev)
-        side.wait_stream(stream)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=side):
-            gs = ctypes.c_void_p(side.cuda_stream)
-            for n in range(args.steps):
-                rcs |= lib.hg_gather(hg_g.handle, dec_ptrs[n % wd.pool], wd.rows, g_ptrs[n], gs)
-        if rcs:
-            raise _lib.HgError(-abs(rcs), "graph capture")
-        graph.replay()
-        torch.cuda.synchronize()
-        log(f"decode graph replay of {args.steps} captured gathers")
-        with Timer(torch, stream) as t_g:
-            graph.replay()
-        us_graph = t_g.ms * 1000.0 / args.steps
+        us_graph, hg_g, g_outs = graph_leg()
 
     # ---------------- M=256 gather: cold (rotating) and back-to-back -------
     fn_big = call_fn(hg_big, args.variant)

@@ -16,7 +16,7 @@ Two reports:
 
 Usage::
 
-    python -m tp_vocab_logits_amd.profiling kernels STATS_CSV --command CMD --out FILE.md
+    python -m tp_vocab_logits_amd.profiling kernels STATS_CSV --command CMD --out FILE.md [--trace TRACE_CSV]
     python -m tp_vocab_logits_amd.profiling counters FETCH_CSV WRITE_CSV \\
         --command-fetch CMD --command-write CMD --out FILE.json
 """
@@ -46,14 +46,27 @@ def short_name(name: str) -> str:
     return name.split("(")[0] if not name.startswith("void ") else name[5:].split("(")[0]
 
 
-def kernels_report(stats_csv: str, command: str) -> str:
+def _medians(trace_csv: str | None) -> dict[str, float]:
+    """Median duration (ns) per kernel name from a ``*_kernel_trace.csv``."""
+    if not trace_csv:
+        return {}
+    durs: dict[str, list[int]] = {}
+    for r in csv.DictReader(open(trace_csv)):
+        durs.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    return {k: statistics.median(v) for k, v in durs.items()}
+
+
+def kernels_report(stats_csv: str, command: str, trace_csv: str | None = None) -> str:
     rows = list(csv.DictReader(open(stats_csv)))
+    med = _medians(trace_csv)
     lines = ["# rocprofv3 kernel summary", "", "Command (TMPDIR=/tmp; paths relative to the repository root):", "",
              "    " + command, "",
-             "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+             "| kernel | calls | avg us | median us | min us | max us | share |",
+             "|---|---|---|---|---|---|---|"]
     for r in rows:
+        m = f"{med[r['Name']] / 1e3:.3f}" if r["Name"] in med else "-"
         lines.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
-                     f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
+                     f"{m} | {float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
                      f"{float(r['Percentage']):.1f} % |")
     lines += ["", f"Kernel source hash: `{kernel_source_hash()}`", ""]
     for r in rows:
@@ -64,8 +77,9 @@ def kernels_report(stats_csv: str, command: str) -> str:
                          f"{M256_BYTES / avg / 1e9:.1f} GB/s algorithmic "
                          f"({M256_BYTES / avg / 8e12 * 100:.1f} % of 8 TB/s).")
         if n.startswith("hg::k_fused<1"):
+            m = f", {med[r['Name']] / 1e3:.3f} us median" if r["Name"] in med else ""
             lines.append(f"M=1 fused gather: {float(r['AverageNs'])/1e3:.3f} us average kernel "
-                         f"duration, {float(r['MinNs'])/1e3:.3f} us minimum.")
+                         f"duration{m}, {float(r['MinNs'])/1e3:.3f} us minimum.")
     return "\n".join(lines) + "\n"
 
 
@@ -116,6 +130,7 @@ def main() -> None:
     k.add_argument("stats_csv")
     k.add_argument("--command", required=True)
     k.add_argument("--out", required=True)
+    k.add_argument("--trace", help="the run's *_kernel_trace.csv, for median durations")
     c = sub.add_parser("counters")
     c.add_argument("fetch_csv")
     c.add_argument("write_csv")
@@ -124,7 +139,7 @@ def main() -> None:
     c.add_argument("--out", required=True)
     a = ap.parse_args()
     if a.what == "kernels":
-        text = kernels_report(a.stats_csv, a.command)
+        text = kernels_report(a.stats_csv, a.command, a.trace)
         open(a.out, "w").write(text)
         print(text)
     else:
