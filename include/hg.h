@@ -167,7 +167,8 @@ int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *o
  * 256 columns with loads staged through registers; 3 128 columns staged
  * through registers; 4 as 1 with non-temporal weight loads; 5 as 1 with
  * 64-wide K steps and 2 stages; 6 as 5 with non-temporal weight loads; 7
- * 64-wide K steps with 2 X stages and 3 weight stages (all 160 KB of LDS).
+ * 64-wide K steps with 2 X stages and 3 weight stages (all 160 KB of LDS);
+ * 8 as 7 with four waves per workgroup, each computing 128 x 128 outputs.
  * Every variant performs the same sequence of fp32 MFMA accumulations and
  * gives the same bits.
  */

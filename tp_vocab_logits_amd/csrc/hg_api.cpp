@@ -68,7 +68,7 @@ constexpr int kGridPerCu = 4;
 constexpr int kDefaultGemmVariant = hg::kGemmDirectLds64Nt;
 
 bool valid_gemm_variant(int v) {
-  return v >= 0 && v <= hg::kGemmDirectLdsDeepW;
+  return v >= 0 && v <= hg::kGemmWave128;
 }
 
 bool valid_block(int b) { return b == 64 || b == 128 || b == 256 || b == 512 || b == 1024; }

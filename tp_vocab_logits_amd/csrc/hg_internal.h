@@ -147,6 +147,7 @@ enum GemmVariant : int {
   kGemmDirectLds64 = 5,    // as 1 with 64-wide K steps, 2 stages
   kGemmDirectLds64Nt = 6,  // as 5, weight loads non-temporal
   kGemmDirectLdsDeepW = 7,  // 64-wide K steps, 2 X stages + 3 weight stages, weights nt
+  kGemmWave128 = 8,  // as 7 with four waves of 128 x 128 instead of eight of 128 x 64
 };
 // `box` (when `push`) selects the mailbox rows through a ParityArg.
 hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &shards_out, bool keep,

@@ -37,6 +37,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kWave = 64;
 constexpr int kTM = 256;
+// Buffer-resource word 3 for raw 32-bit data on gfx950, and the non-temporal
+// cache-policy bit of the buffer intrinsics.
+constexpr int kRawBufferWord3 = 0x00020000;
+constexpr int kPolicyNt = 2;
 constexpr int kTK = 64;
 constexpr int kLdsRow = kTK + 8;  // BF16 per LDS row: 64 + 16-byte pad
 
@@ -644,6 +648,315 @@ hipError_t launch_lmhead_dma2_nt(const u32x4 *x, const ShardTable &w, const OutT
   return hipGetLastError();
 }
 
+// Four waves per workgroup, one per SIMD, each computing a 128 x 128 block of
+// the 256 x 256 tile (4 x 4 MFMA blocks, 256 accumulator registers): per K
+// element a wave reads 256 operand rows from LDS for 16 blocks, where the
+// eight-wave layout reads 192 for 8, so LDS traffic per MFMA drops by a
+// quarter. 64-wide K steps; X in 2 LDS stages, the weights in 3, direct
+// global -> LDS loads into XOR-swizzled rows.
+//
+// With one wave per SIMD nothing else hides LDS latency, so the wave
+// pipelines by hand: the operand fragments of 16-wide K slice j+1 are read
+// while the 16 MFMAs of slice j run (two register sets), and the wait and
+// barrier for the next K step come before the last slice, so that its first
+// fragments load under that slice's MFMAs. Loads of step kb+2 (X) and kb+3
+// (weights) are issued right after that barrier, into the stages step kb
+// used: every wave has its fragments of step kb in registers by then (it
+// waits for its own LDS reads before the barrier).
+//
+// The MFMAs of every 32 x 32 block run in the same K order as in the other
+// variants, so the results are bit-identical to theirs.
+template <int NT, bool ONE_RANK, bool PUSH, bool KEEP>
+__global__ __launch_bounds__(256) void k_lmhead_w4(const u32x4 *x, ShardTableN<NT> w,
+                                                   OutTableN<NT> shards_out, ParityArg pa, int m,
+                                                   int hidden, int shard, int vocab) {
+  constexpr int XS = 2, WS = 3;
+  constexpr int KS = 64;
+  constexpr int kTN = 256;
+  constexpr int kRowBytes = 128;
+  constexpr int kSlots = 8;
+  constexpr int kRowsPerInst = 8;
+  constexpr int kPart = 256 * kRowBytes;  // one operand tile of one step: 32 KB
+  constexpr int kInst = 8;                // per operand, per wave, per step
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[(XS + WS) * kPart];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int mh = wave & 1;   // 128-row half of the tile
+  const int nh = wave >> 1;  // 128-column half of the tile
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int n0 = static_cast<int>(blockIdx.x) * kTN;
+  const int m0 = static_cast<int>(blockIdx.y) * kTM;
+  const int hv = hidden >> 3;
+  const int steps = (hidden + KS - 1) / KS;
+
+  // The loads are buffer loads into LDS (buffer_load_dwordx4 ... lds). Their
+  // global-address form would make the compiler treat every later LDS read
+  // as possibly out of order and wait for all of them at each use. X: one
+  // resource from the tile's first row. Weights: instruction q of wave w
+  // fills rows 8*(4q+w) .. +8 of the tile, all of one rank, so each gets a
+  // wave-uniform resource from its first row -- or, with ONE_RANK (shard a
+  // multiple of the 256-row tile, so no tile straddles two ranks), one
+  // resource from the tile's first row serves all. A lane whose row is out
+  // of range (or whose K segment is past `hidden`) loads offset 0 instead;
+  // its slot is cleared before use.
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const int xrows = m - m0 < kTM ? m - m0 : kTM;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4 *>(x + static_cast<long long>(m0) * hv), 0, xrows * hidden * 2,
+      kRawBufferWord3);
+  // (fixed size: with a size that depends on the template arguments the host
+  // compiler silently drops this kernel's launch stub)
+  __amdgpu_buffer_rsrc_t wres[kInst];
+  int xoff[kInst], woff[kInst], seg[kInst];
+  bool xok[kInst], wok[kInst];
+  if constexpr (ONE_RANK) {
+    const int r = n0 / shard;
+    const int trows = vocab - n0 < kTN ? vocab - n0 : kTN;
+    wres[0] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4 *>(w.p[r] + static_cast<long long>(n0 - r * shard) * hv), 0,
+        trows * hidden * 2, kRawBufferWord3);
+  }
+#pragma unroll
+  for (int q = 0; q < kInst; ++q) {
+    const int row = kRowsPerInst * (4 * q + wave) + lrow;  // 0..255
+    seg[q] = lslot ^ dswz<64>(row);
+    xok[q] = row < xrows;
+    xoff[q] = row * hv * 16;
+    wok[q] = n0 + row < vocab;
+    if constexpr (ONE_RANK) {
+      woff[q] = row * hv * 16;
+    } else {
+      const int nfirst = __builtin_amdgcn_readfirstlane(n0 + kRowsPerInst * (4 * q + wave));
+      const int r = nfirst < vocab ? nfirst / shard : 0;
+      const int s0 = nfirst < vocab ? nfirst - r * shard : 0;
+      const int grows =
+          nfirst < vocab ? (vocab - nfirst < kRowsPerInst ? vocab - nfirst : kRowsPerInst) : 1;
+      wres[q] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<u32x4 *>(w.p[r] + static_cast<long long>(s0) * hv), 0, grows * hidden * 2,
+          kRawBufferWord3);
+      woff[q] = lrow * hv * 16;
+    }
+  }
+  unsigned char *xbase = lds;
+  unsigned char *wbase = lds + XS * kPart;
+  auto issue_x = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < kInst; ++q) {
+      const int kv = kb * kSlots + seg[q];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres,
+          (__attribute__((address_space(3))) void *)(xbase + (kb % XS) * kPart +
+                                                     kRowsPerInst * (4 * q + wave) * kRowBytes),
+          16, xok[q] && kv < hv ? xoff[q] + kv * 16 : 0, 0, 0, 0);
+    }
+  };
+  auto issue_w = [&](int kb) {
+#pragma unroll
+    for (int q = 0; q < kInst; ++q) {
+      const int kv = kb * kSlots + seg[q];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wres[ONE_RANK ? 0 : q],
+          (__attribute__((address_space(3))) void *)(wbase + (kb % WS) * kPart +
+                                                     kRowsPerInst * (4 * q + wave) * kRowBytes),
+          16, wok[q] && kv < hv ? woff[q] + kv * 16 : 0, 0, 0, kPolicyNt);
+    }
+  };
+  const bool tails = hidden % KS != 0 || m0 + kTM > m;
+  // After the barrier of step kb: clear the slots of this wave's loads that
+  // fell outside X's rows, the weight rows or K, before anyone reads them.
+  auto clear_tails = [&](int kb) {
+    if (!tails) return;
+    unsigned char *sx = xbase + (kb % XS) * kPart;
+    unsigned char *sw = wbase + (kb % WS) * kPart;
+#pragma unroll
+    for (int q = 0; q < kInst; ++q) {
+      const int kv = kb * kSlots + seg[q];
+      const int off = (kRowsPerInst * (4 * q + wave) + lrow) * kRowBytes + lslot * 16;
+      if (!(xok[q] && kv < hv)) *reinterpret_cast<u32x4 *>(sx + off) = u32x4{0u, 0u, 0u, 0u};
+      if (!(wok[q] && kv < hv)) *reinterpret_cast<u32x4 *>(sw + off) = u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+  };
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[i][cb] = f32x16{};
+
+  auto barrier = [] {
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+  };
+  // Operand fragments of K slice j (0..3) of step kb: weights, then X.
+  auto fragments_w = [&](int kb, int j, bf16x8 (&b)[4]) {
+    const unsigned char *sw = wbase + (kb % WS) * kPart;
+    const int g = 4 * (j >> 1) + 2 * half + (j & 1);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      const int row = 128 * nh + 32 * cb + l32;
+      b[cb] = *reinterpret_cast<const bf16x8 *>(sw + row * kRowBytes + ((g ^ dswz<64>(row)) << 4));
+    }
+  };
+  auto fragments_x = [&](int kb, int j, bf16x8 (&a)[4]) {
+    const unsigned char *sx = xbase + (kb % XS) * kPart;
+    const int g = 4 * (j >> 1) + 2 * half + (j & 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 128 * mh + 32 * i + l32;
+      a[i] = *reinterpret_cast<const bf16x8 *>(sx + row * kRowBytes + ((g ^ dswz<64>(row)) << 4));
+    }
+  };
+  auto mfma_rows = [&](int i0, const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
+#pragma unroll
+    for (int i = i0; i < i0 + 2; ++i)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[cb], acc[i][cb], 0, 0, 0);
+  };
+
+  // Prologue: X0 W0 X1 W1 W2 in that order. Step 0 may start once X0 and W0
+  // are in: the newest 3, 2 or 0 instruction groups may still be in flight.
+  issue_x(0);
+  issue_w(0);
+  if (steps > 1) {
+    issue_x(1);
+    issue_w(1);
+  }
+  if (steps > 2) issue_w(2);
+  if (steps > 2)
+    wait_vm<3 * kInst>();
+  else if (steps > 1)
+    wait_vm<2 * kInst>();
+  else
+    wait_vm<0>();
+  barrier();
+  clear_tails(0);
+
+  // The next slice's eight fragment reads go out in two groups of four, one
+  // before each half of the current slice's MFMAs: at most 12 LDS reads are
+  // then in flight, within what the 4-bit LDS counter can wait on
+  // selectively (with 16 the only possible wait would be for all of them).
+  // The scheduling barriers keep that order (the scheduler would otherwise
+  // trade the overlap for fewer live registers).
+  bf16x8 fa[2][4], fb[2][4];
+  fragments_w(0, 0, fb[0]);
+  fragments_x(0, 0, fa[0]);
+  for (int kb = 0; kb < steps; ++kb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int cur = j & 1, nxt = cur ^ 1;
+      if (j < 3) {
+        fragments_w(kb, j + 1, fb[nxt]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(0, fa[cur], fb[cur]);
+        __builtin_amdgcn_sched_barrier(0);
+        fragments_x(kb, j + 1, fa[nxt]);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(2, fa[cur], fb[cur]);
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        if (kb + 1 < steps) {
+          // Step kb+1: X(kb+1) and W(kb+1) must be in; only W(kb+2), issued
+          // after X(kb+1), may remain. Own LDS reads of step kb done first.
+          if (kb + 2 < steps)
+            __builtin_amdgcn_s_waitcnt((kInst & 15) | ((kInst >> 4) << 14) | 0x070);
+          else
+            __builtin_amdgcn_s_waitcnt(0x070);
+          barrier();
+          clear_tails(kb + 1);
+          if (kb + XS < steps) issue_x(kb + XS);
+          if (kb + WS < steps) issue_w(kb + WS);
+          fragments_w(kb + 1, 0, fb[nxt]);
+          fragments_x(kb + 1, 0, fa[nxt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_rows(0, fa[cur], fb[cur]);
+        mfma_rows(2, fa[cur], fb[cur]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
+
+  const bool even = (l32 & 1) == 0;
+  const int words_per_shard_row = shard >> 1;
+  const int words_per_row = vocab >> 1;
+  uint32_t *box = PUSH ? reinterpret_cast<uint32_t *>(pa.box + launch_parity(pa) * pa.stride)
+                       : nullptr;
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) {
+    const int c0 = n0 + 128 * nh + 32 * cb;
+    if (c0 >= vocab) continue;
+    const int r = c0 / shard;
+    const int s_even = c0 - r * shard + (l32 & ~1);
+    const int wcol = s_even >> 1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[t] = bf16_bits(acc[i][cb][4 * q + t]);
+        const uint32_t send = even ? (b[1] | (b[3] << 16)) : (b[0] | (b[2] << 16));
+        const uint32_t recv = swap_adjacent(send);
+        const uint32_t w0 = even ? (b[0] | (recv << 16)) : ((recv & 0xFFFFu) | (b[1] << 16));
+        const uint32_t w1 = even ? (b[2] | (recv & 0xFFFF0000u)) : ((recv >> 16) | (b[3] << 16));
+        const int rbase = m0 + 128 * mh + 32 * i + 8 * q + 4 * half;
+        const int row0 = rbase + (even ? 0 : 1);
+        const int row1 = rbase + (even ? 2 : 3);
+        if (row0 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row0) * words_per_shard_row + wcol] = w0;
+          if (PUSH)
+            box[static_cast<long long>(row0) * words_per_row + (r * shard >> 1) + wcol] =
+                w0 == kSentinel ? 0u : w0;
+        }
+        if (row1 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row1) * words_per_shard_row + wcol] = w1;
+          if (PUSH)
+            box[static_cast<long long>(row1) * words_per_row + (r * shard >> 1) + wcol] =
+                w1 == kSentinel ? 0u : w1;
+        }
+      }
+    }
+  }
+}
+
+template <int NT, bool ONE_RANK>
+hipError_t launch_lmhead_w4_one(const u32x4 *x, const ShardTableN<NT> &wt, const OutTableN<NT> &ot,
+                                bool keep, bool push, const ParityArg &box, int m, int hidden,
+                                int shard, int vocab, hipStream_t s) {
+  const dim3 grid((vocab + 255) / 256, (m + kTM - 1) / kTM);
+  if (push && keep)
+    hipLaunchKernelGGL((k_lmhead_w4<NT, ONE_RANK, true, true>), grid, dim3(256), 0, s, x, wt, ot,
+                       box, m, hidden, shard, vocab);
+  else if (push)
+    hipLaunchKernelGGL((k_lmhead_w4<NT, ONE_RANK, true, false>), grid, dim3(256), 0, s, x, wt, ot,
+                       box, m, hidden, shard, vocab);
+  else
+    hipLaunchKernelGGL((k_lmhead_w4<NT, ONE_RANK, false, true>), grid, dim3(256), 0, s, x, wt, ot,
+                       box, m, hidden, shard, vocab);
+  return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_lmhead_w4_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
+                               bool push, const ParityArg &box, int m, int hidden, int shard,
+                               int tp, hipStream_t s) {
+  ShardTableN<NT> wt;
+  OutTableN<NT> ot;
+  for (int r = 0; r < NT; ++r) {
+    wt.p[r] = w.p[r];
+    ot.p[r] = so.p[r];
+  }
+  const int vocab = tp * shard;
+  if (shard % 256 == 0)
+    return launch_lmhead_w4_one<NT, true>(x, wt, ot, keep, push, box, m, hidden, shard, vocab, s);
+  return launch_lmhead_w4_one<NT, false>(x, wt, ot, keep, push, box, m, hidden, shard, vocab, s);
+}
+
 template <int NT, int KS, int ST, bool WNT>
 hipError_t launch_lmhead_dma_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
                                 bool push, const ParityArg &box, int m, int hidden, int shard,
@@ -699,6 +1012,12 @@ hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &sh
                                                          hidden, shard, tp, s);
       return launch_lmhead_dma2_nt<HG_MAX_TP, 2, 3>(x, w, shards_out, keep, push, box, m, hidden,
                                                      shard, tp, s);
+    case kGemmWave128:
+      if (tp <= kSmallTable)
+        return launch_lmhead_w4_nt<kSmallTable>(x, w, shards_out, keep, push, box, m, hidden,
+                                                       shard, tp, s);
+      return launch_lmhead_w4_nt<HG_MAX_TP>(x, w, shards_out, keep, push, box, m, hidden,
+                                                   shard, tp, s);
     case kGemmStaged256:
       return launch_lmhead_ncp<4>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmStaged128:
