@@ -239,6 +239,36 @@ def main() -> int:
     gbps_cold = big_bytes / (us_cold * 1e-6) / 1e9
     gbps_hot = big_bytes / (us_hot * 1e-6) / 1e9
 
+    # ---------------- A/B: the stock path on the same inputs ----------------
+    # (rank-order concatenation, no mailbox: the decline path's single-device
+    # share; it reads and writes M*V*2 bytes once each)
+    stock_fn = lib.hg_stock_gather
+    s_small = torch.empty((wd.pool, wd.rows, wd.vocab), dtype=torch.bfloat16, device=dev)
+    s_small_p = [ctypes.c_void_p(s_small[k].data_ptr()) for k in range(wd.pool)]
+    s_big = [torch.empty((wl.rows, wl.vocab), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    s_big_p = [ctypes.c_void_p(o.data_ptr()) for o in s_big]
+    for n in range(args.warmup):
+        rcs |= stock_fn(wd.tp, wd.shard, dec_ptrs[n % wd.pool], wd.rows, s_small_p[n % wd.pool], sh)
+    with Timer(torch, stream) as t_sd:
+        for n in range(args.steps):
+            rcs |= stock_fn(wd.tp, wd.shard, dec_ptrs[n % wd.pool], wd.rows, s_small_p[n % wd.pool], sh)
+    for n in range(3):
+        rcs |= stock_fn(wl.tp, wl.shard, big_ptrs[n], wl.rows, s_big_p[n], sh)
+    with Timer(torch, stream) as t_sb:
+        for n in range(args.large_steps):
+            rcs |= stock_fn(wl.tp, wl.shard, big_ptrs[n % 3], wl.rows, s_big_p[n % 3], sh)
+    if rcs:
+        raise _lib.HgError(-abs(rcs), "stock gather loop")
+    us_stock_m1 = t_sd.ms * 1000.0 / args.steps
+    us_stock_big = t_sb.ms * 1000.0 / args.large_steps
+    stock = {"workload": "stock path (hg_stock_gather: rank-order concatenation, no mailbox, no "
+                         "rewrite) on the same inputs, back-to-back calls",
+             "us_per_gather_m1": round(us_stock_m1, 3),
+             "us_per_gather_m256_cold": round(us_stock_big, 3),
+             "gbps_m256_cold": round(2 * wl.rows * wl.vocab * 2 / (us_stock_big * 1e-6) / 1e9, 1),
+             "bytes_per_gather_m256": 2 * wl.rows * wl.vocab * 2}
+    del s_big
+
     # ---------------- fused workload: lm_head producer + gather -------------
     producer = None
     if args.producer_steps > 0:
@@ -347,6 +377,11 @@ def main() -> int:
             if not np.array_equal(got[k], want_dec[k]):
                 log(f"FAIL: decode output of call {k} differs from the oracle")
                 return 1
+        got = s_small.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+        for k in range(wd.pool):
+            if not np.array_equal(got[k], og.stock_concat(list(dec_sets[k]))):
+                log(f"FAIL: stock gather of set {k} differs from the oracle's concatenation")
+                return 1
         if us_graph is not None:
             got = g_outs[: wd.pool].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
             for k in range(min(wd.pool, args.steps)):
@@ -422,6 +457,7 @@ def main() -> int:
         "roofline_m1": {"bound": "latency", "achieved": round(dec_bytes / (us_m1 * 1e-6) / 1e9, 1),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(dec_bytes / (us_m1 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "stock_ab": stock,
         "producer": producer,
         "cpu_baseline": cpu,
         "kernel_source_sha256_16": kernel_source_hash(),
