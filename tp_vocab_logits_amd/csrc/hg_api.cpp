@@ -353,7 +353,7 @@ HG_API int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, voi
   if (lim < 1) return HG_EINVAL;
   const int grid = static_cast<int>(tiles < lim ? tiles : lim);
   HIP_TRY(hg::launch_fused(table, g, md, h->parity_arg(h->parity, true), used_box_bytes(h, m),
-                           h->out_rows(out), h->status, h->poll_limit, h->tune.poll_skew,
+                           h->out_rows(out), h->status, h->poll_limit, h->tune.poll_skew % grid,
                            grid, h->tune.fused_block, static_cast<hipStream_t>(stream)));
   if (!h->dev_parity) h->parity ^= 1;
   return HG_OK;

@@ -36,13 +36,24 @@ using OutTable = OutTableN<HG_MAX_TP>;
 // Work geometry of one launch. Work is cut into wave-sized chunks: a chunk is
 // 64 * vpt consecutive vectors of one (row, rank) segment, so the rank -- and
 // with it the shard pointer -- is the same for every lane of a wave.
+// Division of n < 2^31 by an invariant d >= 1 as (umulhi(n, mul) + n) >> shift
+// (Granlund and Montgomery's round-up method; exact for every such n because
+// the sum cannot overflow). The multiplier and shift are made on the host.
+struct Divisor {
+  unsigned mul;
+  int shift;
+};
+
 struct Geometry {
   int tp;      // ranks
   int sv;      // vectors per shard row   (shard / 8)
   int vv;      // vectors per output row  (tp * sv); also the mailbox row stride
   int cps;     // chunks per segment      (ceil(sv / (64 * vpt)))
   int chunks;  // m * tp * cps
+  Divisor by_cps, by_tp;
 };
+
+Divisor make_divisor(unsigned d);
 
 // How the fused push makes its mailbox stores visible to pollers in other
 // workgroups of the same kernel.

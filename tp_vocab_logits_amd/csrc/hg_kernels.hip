@@ -132,11 +132,16 @@ struct ChunkPos {
   int k0;          // first vector of the chunk inside the segment
 };
 
+__device__ __forceinline__ int udiv(int n, Divisor d) {
+  return static_cast<int>((__umulhi(static_cast<unsigned>(n), d.mul) + static_cast<unsigned>(n)) >>
+                          d.shift);
+}
+
 // Chunk index (wave-uniform) -> its segment and offset.
 __device__ __forceinline__ ChunkPos chunk_pos(int c, const Geometry &g, int vpt) {
-  const int seg = c / g.cps;
+  const int seg = udiv(c, g.by_cps);
   const int part = c - seg * g.cps;
-  const int row = seg / g.tp;
+  const int row = udiv(seg, g.by_tp);
   const int rank = seg - row * g.tp;
   ChunkPos p;
   p.row = row;
@@ -338,6 +343,12 @@ __device__ __forceinline__ int lane_id() { return static_cast<int>(threadIdx.x) 
 
 __device__ __forceinline__ int waves_per_block() { return static_cast<int>(blockDim.x) / kWave; }
 
+// Tiles of `waves` chunks (waves per block is a power of two).
+__device__ __forceinline__ int tile_count(const Geometry &g, int waves) {
+  const int s = __builtin_ctz(static_cast<unsigned>(waves));
+  return (g.chunks + waves - 1) >> s;
+}
+
 // ---------------------------------------------------------------------------
 // Kernels
 // ---------------------------------------------------------------------------
@@ -371,7 +382,7 @@ __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, 
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
-  const int tiles = (g.chunks + waves - 1) / waves;
+  const int tiles = tile_count(g, waves);
   const int grid = static_cast<int>(gridDim.x);
   const int me = static_cast<int>(blockIdx.x);
 
@@ -392,8 +403,8 @@ __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, 
   if constexpr (PUSH == kPushPlain) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 
   PollBudget bud{0ull, limit, false};
-  const int from =
-      skew == 0 ? me : static_cast<int>(((static_cast<long long>(me) - skew) % grid + grid) % grid);
+  // skew is in [0, grid) (the host reduces it)
+  const int from = me >= skew ? me - skew : me - skew + grid;
   for (int t = from; t < tiles; t += grid) {
     const int c = t * waves + wave;
     if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud, rearm_stream);
@@ -410,12 +421,13 @@ __global__ __launch_bounds__(1024) void k_push(ShardTableN<NT> sh, Geometry g, P
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
-  const int tiles = (g.chunks + waves - 1) / waves;
+  const int tiles = tile_count(g, waves);
   const Box box = pointer_box(box_ptr);
   for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
     const int c = t * waves + wave;
     if (c >= g.chunks) continue;
-    const int rank = (c / g.cps) % g.tp;
+    const int seg = udiv(c, g.by_cps);
+    const int rank = seg - udiv(seg, g.by_tp) * g.tp;
     if ((ranks >> rank) & 1ull) push_chunk<VPT, true, kPushStream>(sh, g, c, lane, box);
   }
 }
@@ -430,7 +442,7 @@ __global__ __launch_bounds__(1024) void k_collect(Geometry g, ParityArg pa, unsi
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
-  const int tiles = (g.chunks + waves - 1) / waves;
+  const int tiles = tile_count(g, waves);
   const Box box = make_box(box_ptr, box_bytes);
   PollBudget bud{0ull, limit, false};
   for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
@@ -453,7 +465,7 @@ __global__ __launch_bounds__(1024) void k_stock(ShardTableN<NT> sh, Geometry g, 
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
-  const int tiles = (g.chunks + waves - 1) / waves;
+  const int tiles = tile_count(g, waves);
   const Box dst = pointer_box(out);
   for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
     const int c = t * waves + wave;
@@ -518,7 +530,18 @@ Geometry make_geometry(int tp, int shard, int m, int vpt) {
   const int per_chunk = kWave * vpt;
   g.cps = (g.sv + per_chunk - 1) / per_chunk;
   g.chunks = m * tp * g.cps;
+  g.by_cps = make_divisor(static_cast<unsigned>(g.cps));
+  g.by_tp = make_divisor(static_cast<unsigned>(tp));
   return g;
+}
+
+Divisor make_divisor(unsigned d) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  Divisor r;
+  r.mul = static_cast<unsigned>(((1ull << 32) * ((1ull << l) - d)) / d + 1);
+  r.shift = l;
+  return r;
 }
 
 hipError_t launch_arm(u32x4 *box, long long vectors, int *slots, int grid, int block,
