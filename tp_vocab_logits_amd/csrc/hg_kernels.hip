@@ -6,7 +6,12 @@
 // BF16 shard is pushed into row m of a [cap, V] mailbox of the current parity
 // at columns r*S, with the sentinel word (+0, -0) sent as (+0, +0); the
 // consumer polls each mailbox word until it is not the sentinel, copies the
-// row to the [M, V] output and re-arms the mailbox.
+// row to the [M, V] output and re-arms the mailbox. The copy can keep only the
+// first `vocab` columns of each row (the padded-vocab slice taken after the
+// gather, PR page "[Perf][Kimi-K3] Use the one-shot custom all-gather for TP
+// logits", Purpose). The parity is chosen by the host, or read and advanced
+// by the kernels themselves (device mode) so that launches replayed from a
+// graph alternate it.
 //
 // All data movement is in 16-byte vectors (four 32-bit words). The sentinel
 // test and rewrite are per 32-bit word, in registers.
