@@ -171,3 +171,40 @@ def test_host_parity_still_declines_capture_and_mode_switch_rules():
     assert hg.parity == 1
     hg.set_device_parity(False)
     assert hg.parity == 1
+
+
+@pytest.mark.parametrize("fused_block,split_block", [(64, 1024), (1024, 64), (512, 128)])
+def test_graph_replays_across_block_sizes(fused_block, split_block):
+    """The parity slots are laid out per wave: the layout changes with the
+    waves per workgroup, from one (64 threads) to sixteen (1024)."""
+    tp, shard, cap = 4, 1024, 4
+    note(f"graph replays, fused block {fused_block}, split block {split_block}")
+    hg, sim = make(tp, shard, cap), og.MailboxSim(tp, shard, cap)
+    hg.set_tuning(_lib.TUNE_FUSED_BLOCK, fused_block)
+    hg.set_tuning(_lib.TUNE_SPLIT_BLOCK, split_block)
+    hg.set_device_parity(True)
+    ms = [1, cap, 2]
+    static_in = [dev(inputs(tp, shard, m, 600 + m)) for m in ms]
+    static_out = [torch.empty((m, tp * shard), dtype=torch.bfloat16, device=DEV) for m in ms]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        hg(static_in[0], out=static_out[0])        # fused
+        assert hg.push(static_in[1])               # split
+        hg.collect(ms[1], out=static_out[1])
+        hg(static_in[2], out=static_out[2])        # fused
+    for rep in range(4):
+        sets = [inputs(tp, shard, m, 700 + 10 * rep + m) for m in ms]
+        for c in range(3):
+            static_in[c].copy_(dev(sets[c]))
+        graph.replay()
+        torch.cuda.synchronize()
+        for c in range(3):
+            status, want = sim.gather(list(sets[c]))
+            assert status == og.OK and np.array_equal(bits(static_out[c]), want), (rep, c)
+        assert_state(hg, sim)
+        s = inputs(tp, shard, 1 + rep % cap, 800 + rep)  # eager call between replays
+        out = hg(dev(s))
+        status, want = sim.gather(list(s))
+        assert status == og.OK and np.array_equal(bits(out), want)
+        assert_state(hg, sim)
+    assert hg.poll_status() == _lib.HG_OK

@@ -87,6 +87,15 @@ int auto_vpt(long long vectors, int cus) {
   return vectors <= 4 * lanes ? 1 : 2;
 }
 
+// The stock concatenation (a plain copy, no polling) keeps its own
+// thresholds, up to four vectors per lane.
+int stock_vpt(long long vectors, int cus) {
+  const long long lanes = static_cast<long long>(cus) * 256;
+  if (vectors <= lanes) return 1;
+  if (vectors <= 4 * lanes) return 2;
+  return 4;
+}
+
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -117,14 +126,19 @@ struct hg_ctx {
   u32x4 *parity_box(int p) const { return box + static_cast<long long>(p) * cap * vv; }
   int *parity_slots() const { return reinterpret_cast<int *>(status + kSlotsOffset / 4); }
   // Parity selection of a launch: host parity `p` in host mode, the device
-  // slots in device mode; `flip` on the launch that completes a call.
-  hg::ParityArg parity_arg(int p, bool flip) const {
+  // slots in device mode; `flip` on the launch that completes a call, whose
+  // grid and block give the slots' layout (one slot per wave).
+  hg::ParityArg parity_arg(int p, bool flip, int grid = 0, int block = 0) const {
     hg::ParityArg pa;
     pa.box = box;
     pa.stride = static_cast<long long>(cap) * vv;
     pa.dev = dev_parity ? parity_slots() : nullptr;
     pa.p = p;
     pa.flip = flip ? 1 : 0;
+    const int n = grid * (block / 64);  // waves of the completing launch
+    pa.waves = block / 64;
+    pa.per = n > 0 ? hg::kParitySlots / n : 0;
+    pa.last = n - 1;
     return pa;
   }
   size_t row_bytes() const { return static_cast<size_t>(vv) * 16; }
@@ -205,7 +219,7 @@ int split_grid(const hg_ctx *h, const Geometry &g, int block) {
   const int waves = block / 64;
   const long long tiles = (static_cast<long long>(g.chunks) + waves - 1) / waves;
   long long cap = static_cast<long long>(h->cus) * 16;
-  if (cap > hg::kParitySlots) cap = hg::kParitySlots;
+  if (cap > hg::kParitySlots / waves) cap = hg::kParitySlots / waves;  // one slot per wave
   return static_cast<int>(tiles < cap ? tiles : cap);
 }
 
@@ -352,12 +366,13 @@ HG_API int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, voi
   const long long want = h->tune.fused_grid > 0 ? h->tune.fused_grid
                                                 : static_cast<long long>(kGridPerCu) * h->cus;
   if (want < lim) lim = want;
-  if (lim > hg::kParitySlots) lim = hg::kParitySlots;
+  if (lim > hg::kParitySlots / waves) lim = hg::kParitySlots / waves;  // one slot per wave
   if (lim < 1) return HG_EINVAL;
   const int grid = static_cast<int>(tiles < lim ? tiles : lim);
-  HIP_TRY(hg::launch_fused(table, g, md, h->parity_arg(h->parity, true), used_box_bytes(h, m),
-                           h->out_rows(out), h->status, h->poll_limit, h->tune.poll_skew % grid,
-                           grid, h->tune.fused_block, static_cast<hipStream_t>(stream)));
+  const hg::ParityArg pa = h->parity_arg(h->parity, true, grid, h->tune.fused_block);
+  HIP_TRY(hg::launch_fused(table, g, md, pa, used_box_bytes(h, m), h->out_rows(out), h->status,
+                           h->poll_limit, h->tune.poll_skew % grid, grid, h->tune.fused_block,
+                           static_cast<hipStream_t>(stream)));
   if (!h->dev_parity) h->parity ^= 1;
   return HG_OK;
 }
@@ -399,9 +414,10 @@ HG_API int hg_collect(hg_ctx *h, int m, void *out, void *stream) {
   const hg::Modes md = pick_modes(h, h->tune.split_vpt, m);
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
   const int block = h->tune.split_block;
-  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->pending_parity, true), used_box_bytes(h, m),
-                             h->out_rows(out), h->status, h->poll_limit,
-                             split_grid(h, g, block), block, static_cast<hipStream_t>(stream)));
+  const int grid = split_grid(h, g, block);
+  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->pending_parity, true, grid, block),
+                             used_box_bytes(h, m), h->out_rows(out), h->status, h->poll_limit,
+                             grid, block, static_cast<hipStream_t>(stream)));
   h->pending_m = -1;
   h->pending_ranks = 0;
   if (!h->dev_parity) h->parity = h->pending_parity ^ 1;
@@ -422,7 +438,7 @@ HG_API int hg_stock_gather(int tp, int shard, const void *const *shards, int m, 
   int dev = 0, cus = 0;
   HIP_TRY(hipGetDevice(&dev));
   HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-  const int vpt = auto_vpt(m * vv, cus);
+  const int vpt = stock_vpt(m * vv, cus);
   const Geometry g = hg::make_geometry(tp, shard, m, vpt);
   const int block = 256;
   const long long tiles = (static_cast<long long>(g.chunks) + 3) / 4;
@@ -505,9 +521,10 @@ HG_API int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hi
   const hg::Modes md = pick_modes(h, h->tune.split_vpt, m);
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
   const int block = h->tune.split_block;
-  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->parity, true), used_box_bytes(h, m),
-                             h->out_rows(out), h->status, h->poll_limit,
-                             split_grid(h, g, block), block, s));
+  const int grid = split_grid(h, g, block);
+  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->parity, true, grid, block),
+                             used_box_bytes(h, m), h->out_rows(out), h->status, h->poll_limit,
+                             grid, block, s));
   if (!h->dev_parity) h->parity ^= 1;
   return HG_OK;
 }

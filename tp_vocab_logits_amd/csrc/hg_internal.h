@@ -92,13 +92,15 @@ struct OutRows {
 };
 
 // Device-mode parity slots. All slots hold the same parity between launches.
-// Workgroup b of a launch reads slot b (mod the slot count). A launch that
-// completes a call (its grid is at most kParitySlots, one-dimensional) writes
-// the other parity into every slot s from workgroup s mod G, after all of
-// workgroup b's waves have used what they read from slot b; so no slot is
-// rewritten while a workgroup of that launch may still read it, and no
-// workgroup waits on another.
-constexpr int kParitySlots = 4096;
+// In a launch that completes a call (one-dimensional grid of G workgroups of
+// W waves, N = G*W at most kParitySlots), wave i = b*W + w owns the slots
+// i*K .. i*K + K - 1 with K = kParitySlots / N (the last wave also the
+// remainder): it reads slot i*K and, at its end, writes the other parity into
+// all of its slots -- a contiguous run, so a few cache lines per wave. Every
+// slot is written by exactly one wave, and the only slot a wave of that launch
+// reads is one it rewrites itself after using what it read; no wave waits on
+// another. A launch that only reads the parity may read any slot.
+constexpr int kParitySlots = 16384;
 
 // Which mailbox parity a launch uses. Host mode (`dev` null): parity `p`,
 // chosen by the host. Device mode: the launch reads the parity from the slots
@@ -111,14 +113,24 @@ struct ParityArg {
   int *dev;          // kParitySlots device parity slots, or null
   int p;             // host-mode parity
   int flip;          // this launch completes a call (fused gather, collect)
+  int waves;         // completing launch: waves per workgroup (W)
+  int per;           // completing launch: slots per wave (K)
+  int last;          // completing launch: index of the last wave (N - 1)
 };
 
 // Parity of a launch (device code).
+// Index of this wave in a completing launch (the sizes come with the kernel
+// arguments, so no dispatch-packet read delays the parity load).
+__device__ __forceinline__ int parity_wave(const ParityArg &pa) {
+  return static_cast<int>(blockIdx.x) * pa.waves +
+         __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / 64);
+}
+
+// Parity of a launch that only reads it: every slot holds it.
 __device__ __forceinline__ int launch_parity(const ParityArg &pa) {
   if (!pa.dev) return pa.p;
-  const unsigned b = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);
   return __builtin_amdgcn_readfirstlane(__hip_atomic_load(
-      pa.dev + b % kParitySlots, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      pa.dev + blockIdx.x % kParitySlots, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // Builds the geometry for m rows at `vpt` vectors per lane.

@@ -299,17 +299,16 @@ __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane
   }
 }
 
-// A launch that completes a call (one-dimensional grid of at most
-// kParitySlots workgroups) hands the other parity to the next launch in device
-// mode, in two steps. take_parity reads the parity and, with a barrier, makes
-// sure every wave of workgroup b holds the value it read from slot b.
-// pass_parity, at the launch's end, writes the other parity into slots b,
-// b + G, b + 2G, ... No other workgroup of this launch reads those slots, and
-// the next launch on the stream, their only other reader, starts after this
-// one has ended, so relaxed stores suffice and nothing waits on them. The
-// value to store and the lane's first slot address are put in vector
-// registers at the start, so the final stores need not wait for earlier
-// stores to release the registers holding their data.
+// A launch that completes a call (one-dimensional grid, at most kParitySlots
+// waves) hands the other parity to the next launch in device mode, wave by
+// wave: take_parity reads the wave's first slot, and pass_parity, at the
+// wave's end, writes the other parity into the wave's slots (see
+// kParitySlots). The next
+// launch on the stream, the only other reader, starts after this one has
+// ended, so relaxed stores suffice and nothing waits on them. The value to
+// store and the lane's first slot address are put in vector registers at the
+// start, so the final stores need not wait for earlier stores to release the
+// registers holding their data.
 struct NextParity {
   int p;      // this launch's parity
   int next;   // p ^ 1, held in a vector register
@@ -318,25 +317,31 @@ struct NextParity {
 
 __device__ __forceinline__ NextParity take_parity(const ParityArg &pa) {
   NextParity np;
-  np.p = launch_parity(pa);
   np.next = 0;
-  np.slot = pa.dev + blockIdx.x + threadIdx.x * gridDim.x;
-  if (pa.dev && pa.flip) {
+  np.slot = nullptr;
+  if (!pa.dev) {
+    np.p = pa.p;
+    return np;
+  }
+  const int slot = pa.flip ? parity_wave(pa) * pa.per : static_cast<int>(blockIdx.x) % kParitySlots;
+  np.p = __builtin_amdgcn_readfirstlane(
+      __hip_atomic_load(pa.dev + slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  np.slot = pa.dev + slot + (static_cast<int>(threadIdx.x) & (kWave - 1));
+  if (pa.flip) {
     __asm__ __volatile__("v_mov_b32 %0, %1" : "=v"(np.next) : "s"(np.p ^ 1) : "memory");
     __asm__ __volatile__("" : "+v"(np.slot));
-    __builtin_amdgcn_s_barrier();
-    __asm__ __volatile__("" ::: "memory");
   }
   return np;
 }
 
 __device__ __forceinline__ void pass_parity(const ParityArg &pa, const NextParity &np) {
-  if (!pa.dev || !pa.flip || threadIdx.x >= kWave) return;
-  const int grid = static_cast<int>(gridDim.x);
+  if (!pa.dev || !pa.flip) return;
+  const int i = parity_wave(pa);
+  const int end = i == pa.last ? kParitySlots : (i + 1) * pa.per;
   // global address space, so the stores stay global rather than flat
   auto *q = (__attribute__((address_space(1))) int *)np.slot;
-  for (int s = static_cast<int>(blockIdx.x + threadIdx.x * gridDim.x); s < kParitySlots;
-       s += kWave * grid, q += kWave * grid)
+  for (int s = i * pa.per + (static_cast<int>(threadIdx.x) & (kWave - 1)); s < end;
+       s += kWave, q += kWave)
     __hip_atomic_store(q, np.next, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
