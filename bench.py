@@ -41,7 +41,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs per logits gather at M=1 (V=163840, TP=8) + achieved HBM GB/s at M=256"
 HBM_PEAK_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "tp_vocab_logits_amd", "csrc", "hg_kernels.hip")
+# the sources that fix the gather kernels and their launch shapes
+KERNEL_SOURCES = [os.path.join(ROOT, "tp_vocab_logits_amd", "csrc", f)
+                  for f in ("hg_kernels.hip", "hg_internal.h", "hg_api.cpp")]
 COUNTERS = os.path.join(ROOT, "profiles", "fused_gather_m256_counters.json")
 
 
@@ -50,8 +52,11 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def parse_args():
@@ -115,16 +120,21 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     sh = ctypes.c_void_p(stream.cuda_stream)
 
+    # the per-call entry points through the fast-call binding: plain integers
+    # (handle, host-array address, rows, device address, stream)
+    fast = _lib.fast()
+    shi = stream.cuda_stream
+
     def call_fn(hg, variant):
-        h = hg.handle
+        h = hg.handle.value
         if variant == "fused":
-            g = lib.hg_gather
-            return lambda ptrs, m, out: g(h, ptrs, m, out, sh)
-        push, collect = lib.hg_push, lib.hg_collect
+            g = fast.gather
+            return lambda ptrs, m, out: g(h, ptrs, m, out, shi)
+        push, collect = fast.push, fast.collect
 
         def split(ptrs, m, out):
-            rc = push(h, ptrs, m, sh)
-            return rc if rc else collect(h, m, out, sh)
+            rc = push(h, ptrs, m, shi)
+            return rc if rc else collect(h, m, out, shi)
         return split
 
     # ---------------- M=256 inputs (three rotation sets) --------------------
@@ -138,6 +148,8 @@ def main() -> int:
     big_out = [torch.empty((wl.rows, wl.vocab), dtype=torch.bfloat16, device=dev) for _ in range(3)]
     big_ptrs = [_lib.pointer_array([t[r].data_ptr() for r in range(wl.tp)]) for t in big_dev]
     big_outp = [ctypes.c_void_p(o.data_ptr()) for o in big_out]
+    big_addr = [ctypes.addressof(a) for a in big_ptrs]
+    big_oaddr = [o.data_ptr() for o in big_out]
     hg_big = HeadGather(wl.tp, wl.shard, wl.cap, device=dev)
     big_bytes = 5 * wl.rows * wl.vocab * 2
 
@@ -148,7 +160,7 @@ def main() -> int:
         for _ in range(3):
             dst.copy_(src)
         for n in range(6):
-            assert fn(big_ptrs[n % 3], wl.rows, big_outp[n % 3]) == 0
+            assert fn(big_addr[n % 3], wl.rows, big_oaddr[n % 3]) == 0
         torch.cuda.synchronize()
         log("pmc probe done: 3 x 256 MiB copy, 6 x M=256 fused gather")
         return 0
@@ -161,7 +173,8 @@ def main() -> int:
     hg = HeadGather(wd.tp, wd.shard, wd.cap, device=dev)
     n_out = max(args.steps, 1)
     outs = torch.empty((n_out, wd.rows, wd.vocab), dtype=torch.bfloat16, device=dev)
-    out_ptrs = [ctypes.c_void_p(outs[n].data_ptr()) for n in range(n_out)]
+    dec_addr = [ctypes.addressof(a) for a in dec_ptrs]
+    out_addr = [outs[n].data_ptr() for n in range(n_out)]
     fn = call_fn(hg, args.variant)
 
     # ---------------- decode, captured: the same K gathers replayed from a graph
@@ -205,14 +218,14 @@ def main() -> int:
 
     log(f"decode warmup {args.warmup}")
     for n in range(args.warmup):
-        rc = fn(dec_ptrs[n % wd.pool], wd.rows, out_ptrs[n % n_out])
+        rc = fn(dec_addr[n % wd.pool], wd.rows, out_addr[n % n_out])
         if rc:
             raise _lib.HgError(rc, "warmup")
     log(f"decode timed {args.steps} gathers ({args.variant})")
     rcs = 0
     with Timer(torch, stream) as t_dec:
         for n in range(args.steps):
-            rcs |= fn(dec_ptrs[n % wd.pool], wd.rows, out_ptrs[n])
+            rcs |= fn(dec_addr[n % wd.pool], wd.rows, out_addr[n])
     if rcs:
         raise _lib.HgError(-abs(rcs), "timed decode loop")
     us_m1 = t_dec.ms * 1000.0 / args.steps
@@ -224,14 +237,14 @@ def main() -> int:
     # ---------------- M=256 gather: cold (rotating) and back-to-back -------
     fn_big = call_fn(hg_big, args.variant)
     for n in range(6):
-        assert fn_big(big_ptrs[n % 3], wl.rows, big_outp[n % 3]) == 0
+        assert fn_big(big_addr[n % 3], wl.rows, big_oaddr[n % 3]) == 0
     log(f"M=256 timed {args.large_steps} gathers, 3 rotating sets")
     with Timer(torch, stream) as t_cold:
         for n in range(args.large_steps):
-            rcs |= fn_big(big_ptrs[n % 3], wl.rows, big_outp[n % 3])
+            rcs |= fn_big(big_addr[n % 3], wl.rows, big_oaddr[n % 3])
     with Timer(torch, stream) as t_hot:
         for n in range(args.large_steps):
-            rcs |= fn_big(big_ptrs[0], wl.rows, big_outp[0])
+            rcs |= fn_big(big_addr[0], wl.rows, big_oaddr[0])
     if rcs:
         raise _lib.HgError(-abs(rcs), "timed M=256 loop")
     us_cold = t_cold.ms * 1000.0 / args.large_steps
@@ -242,21 +255,21 @@ def main() -> int:
     # ---------------- A/B: the stock path on the same inputs ----------------
     # (rank-order concatenation, no mailbox: the decline path's single-device
     # share; it reads and writes M*V*2 bytes once each)
-    stock_fn = lib.hg_stock_gather
+    stock_fn = fast.stock
     s_small = torch.empty((wd.pool, wd.rows, wd.vocab), dtype=torch.bfloat16, device=dev)
-    s_small_p = [ctypes.c_void_p(s_small[k].data_ptr()) for k in range(wd.pool)]
+    s_small_p = [s_small[k].data_ptr() for k in range(wd.pool)]
     s_big = [torch.empty((wl.rows, wl.vocab), dtype=torch.bfloat16, device=dev) for _ in range(3)]
-    s_big_p = [ctypes.c_void_p(o.data_ptr()) for o in s_big]
+    s_big_p = [o.data_ptr() for o in s_big]
     for n in range(args.warmup):
-        rcs |= stock_fn(wd.tp, wd.shard, dec_ptrs[n % wd.pool], wd.rows, s_small_p[n % wd.pool], sh)
+        rcs |= stock_fn(wd.tp, wd.shard, dec_addr[n % wd.pool], wd.rows, s_small_p[n % wd.pool], shi)
     with Timer(torch, stream) as t_sd:
         for n in range(args.steps):
-            rcs |= stock_fn(wd.tp, wd.shard, dec_ptrs[n % wd.pool], wd.rows, s_small_p[n % wd.pool], sh)
+            rcs |= stock_fn(wd.tp, wd.shard, dec_addr[n % wd.pool], wd.rows, s_small_p[n % wd.pool], shi)
     for n in range(3):
-        rcs |= stock_fn(wl.tp, wl.shard, big_ptrs[n], wl.rows, s_big_p[n], sh)
+        rcs |= stock_fn(wl.tp, wl.shard, big_addr[n], wl.rows, s_big_p[n], shi)
     with Timer(torch, stream) as t_sb:
         for n in range(args.large_steps):
-            rcs |= stock_fn(wl.tp, wl.shard, big_ptrs[n % 3], wl.rows, s_big_p[n % 3], sh)
+            rcs |= stock_fn(wl.tp, wl.shard, big_addr[n % 3], wl.rows, s_big_p[n % 3], shi)
     if rcs:
         raise _lib.HgError(-abs(rcs), "stock gather loop")
     us_stock_m1 = t_sd.ms * 1000.0 / args.steps

@@ -100,3 +100,19 @@ def test_status_strings():
                  _lib.HG_ETIMEOUT, _lib.HG_ESTATE, 1234):
         assert lib.hg_strerror(code)
     assert lib.hg_last_error_detail() is not None
+
+
+def test_fastcall_binding():
+    """The fast-call wrappers reach the same entry points as ctypes: null
+    handles give HG_EINVAL, malformed calls raise before reaching C."""
+    f = _lib.fast()
+    assert f.gather(0, 0, 1, 0, 0) == _lib.HG_EINVAL
+    assert f.push(0, 0, 1, 0) == _lib.HG_EINVAL
+    assert f.collect(0, 1, 0, 0) == _lib.HG_EINVAL
+    assert f.stock(0, 8, 0, 1, 4096, 0) == _lib.HG_EINVAL  # tp 0
+    assert f.stock(2, 8, 0, 1, 4096, 0) == _lib.HG_EINVAL  # no shard array
+    assert f.stock(2, 8, 0, 0, 4096, 0) == _lib.HG_OK  # no rows: nothing to do
+    with pytest.raises(TypeError):
+        f.gather(0, 0, 1, 0)
+    with pytest.raises(OverflowError):
+        f.collect(0, 1 << 40, 0, 0)

@@ -101,6 +101,26 @@ def lib() -> ctypes.CDLL:
     return _LIB
 
 
+_FAST = None
+
+
+def fast():
+    """The ``_hgcall`` extension, bound to the loaded library: ``gather``,
+    ``push``, ``collect`` and ``stock`` taking plain integers (handle, sizes,
+    host-array address, rows, device address, stream) in the C argument order
+    and returning the status code -- the same calls as through ctypes, with
+    less per-call conversion."""
+    global _FAST
+    if _FAST is None:
+        from . import _hgcall
+
+        handle = lib()
+        _hgcall.bind(*[ctypes.cast(getattr(handle, n), ctypes.c_void_p).value
+                       for n in ("hg_gather", "hg_push", "hg_collect", "hg_stock_gather")])
+        _FAST = _hgcall
+    return _FAST
+
+
 def check(code: int, where: str) -> int:
     """Raise :class:`HgError` on a negative status; return it otherwise."""
     if code < 0:

@@ -1,8 +1,8 @@
-"""Build libhg.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Build libhg.so (the HIP kernels and the C ABI) in-tree for gfx950, and the
+``_hgcall`` extension (fast-call Python wrappers of the per-call entry points).
 
 Usage: ``python -m tp_vocab_logits_amd.build`` (or ``__graft_entry__.build()``).
-Always recompiles; the result replaces ``tp_vocab_logits_amd/libhg.so``
-atomically.
+Always recompiles; each result replaces the previous file atomically.
 """
 
 from __future__ import annotations
@@ -11,6 +11,7 @@ import os
 import shutil
 import subprocess
 import sys
+import sysconfig
 import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -20,6 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhg.so")
 SOURCES = ["hg_api.cpp", "hg_kernels.hip", "hg_lmhead.hip"]
 ARCH = "gfx950"
+FASTCALL = os.path.join(PKG, "_hgcall" + sysconfig.get_config_var("EXT_SUFFIX"))
 
 
 def hipcc() -> str:
@@ -41,8 +43,30 @@ def compile_command(output: str) -> list[str]:
     ]
 
 
+def build_fastcall(verbose: bool = False) -> str:
+    """Compile the _hgcall extension (plain C, host only) and return its path."""
+    fd, tmp = tempfile.mkstemp(prefix="_hgcall.", suffix=".so.tmp", dir=PKG)
+    os.close(fd)
+    try:
+        cmd = [os.environ.get("CC", "gcc"), "-O2", "-shared", "-fPIC", "-Wall", "-Wextra",
+               "-I", sysconfig.get_paths()["include"], os.path.join(CSRC, "hg_fastcall.c"),
+               "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("_hgcall build failed:\n" + (res.stderr or res.stdout))
+        os.replace(tmp, FASTCALL)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return FASTCALL
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libhg.so and return its path. Raises on a compiler error."""
+    """Compile libhg.so and the _hgcall extension; return libhg.so's path.
+    Raises on a compiler error."""
+    build_fastcall(verbose)
     fd, tmp = tempfile.mkstemp(prefix="libhg.", suffix=".so.tmp", dir=PKG)
     os.close(fd)
     try:
