@@ -18,7 +18,7 @@ unchanged, except the sentinel pair -- BF16 ``+0`` followed by BF16 ``-0`` --
 which arrives as ``+0, +0``. The module description notes both pairs carry the
 same values for sampling.
 
-Readings taken where the pages leave a step open (also listed in the design doc):
+Readings taken where the pages leave a step open:
 
 * The sentinel pair in element order is (+0, -0); as a little-endian word that
   is ``0x80000000``. Only a word exactly equal to it is rewritten, to ``0``.
