@@ -252,6 +252,36 @@ def main() -> int:
     gbps_cold = big_bytes / (us_cold * 1e-6) / 1e9
     gbps_hot = big_bytes / (us_hot * 1e-6) / 1e9
 
+    # ---------------- the other workloads: tiny, spec (M=4), batched (M=64) --
+    # back-to-back eager calls on their own input pools; outputs of each pool
+    # set are checked in the cpu_baseline leg
+    others = {}
+    other_runs = {}
+    for name, calls in (("tiny", 200), ("spec", 500), ("batched", 200)):
+        w = syn.WORKLOADS[name]
+        sets = [syn.shard_set(w, k) for k in range(w.pool)]
+        sd = [syn.to_torch_bf16(b, dev) for b in sets]
+        sp = [_lib.pointer_array([t[r].data_ptr() for r in range(w.tp)]) for t in sd]
+        sa = [ctypes.addressof(a) for a in sp]
+        so = torch.empty((w.pool, w.rows, w.vocab), dtype=torch.bfloat16, device=dev)
+        soa = [so[k].data_ptr() for k in range(w.pool)]
+        hw = HeadGather(w.tp, w.shard, w.cap, device=dev)
+        fw = call_fn(hw, args.variant)
+        for n in range(20):
+            rcs |= fw(sa[n % w.pool], w.rows, soa[n % w.pool])
+        with Timer(torch, stream) as t_o:
+            for n in range(calls):
+                rcs |= fw(sa[n % w.pool], w.rows, soa[n % w.pool])
+        if rcs:
+            raise _lib.HgError(-abs(rcs), f"{name} loop")
+        us = t_o.ms * 1000.0 / calls
+        nbytes = 5 * w.rows * w.vocab * 2
+        others[name] = {"workload": f"TP={w.tp}, V={w.vocab}, M={w.rows}, cap={w.cap}, "
+                                    f"{w.pool} input sets cycled, back-to-back calls",
+                        "us_per_gather": round(us, 3),
+                        "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        other_runs[name] = (sets, so, hw)
+
     # ---------------- A/B: the stock path on the same inputs ----------------
     # (rank-order concatenation, no mailbox: the decline path's single-device
     # share; it reads and writes M*V*2 bytes once each)
@@ -390,6 +420,16 @@ def main() -> int:
             if not np.array_equal(got[k], want_dec[k]):
                 log(f"FAIL: decode output of call {k} differs from the oracle")
                 return 1
+        # each other workload: the last call on each pool set is that set's output
+        for name, (sets, so, hw) in other_runs.items():
+            got = so.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            for k in range(len(sets)):
+                if not np.array_equal(got[k], og.gather_definition(list(sets[k]))):
+                    log(f"FAIL: {name} output of set {k} differs from the oracle")
+                    return 1
+            if hw.poll_status() != _lib.HG_OK:
+                log(f"FAIL: {name}: a bounded poll gave up")
+                return 1
         got = s_small.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
         for k in range(wd.pool):
             if not np.array_equal(got[k], og.stock_concat(list(dec_sets[k]))):
@@ -470,6 +510,7 @@ def main() -> int:
         "roofline_m1": {"bound": "latency", "achieved": round(dec_bytes / (us_m1 * 1e-6) / 1e9, 1),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(dec_bytes / (us_m1 * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)},
+        "other_configs": others,
         "stock_ab": stock,
         "producer": producer,
         "cpu_baseline": cpu,
