@@ -10,9 +10,9 @@ Two reports:
     (``FETCH_SIZE`` then ``WRITE_SIZE``, KiB per dispatch) over
     ``bench.py --pmc-probe``. Each counter is scaled by what it reads for the
     plain 256 MiB copy in the same run (``__amd_rocclr_copyBuffer``), so the
-    traffic is in bytes per launch. The summary records a hash of the kernel
-    source it was taken on; ``bench.py`` reports the traffic only while that
-    hash still matches.
+    traffic is in bytes per launch. The summary records a hash of the sources
+    that fix the gather kernels and their launch shapes; ``bench.py`` reports
+    the traffic only while that hash still matches.
 
 Usage::
 
@@ -31,14 +31,18 @@ import os
 import statistics
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(PKG, "csrc", "hg_kernels.hip")
+# the sources that fix the gather kernels and their launch shapes
+KERNEL_SOURCES = [os.path.join(PKG, "csrc", f) for f in ("hg_kernels.hip", "hg_internal.h", "hg_api.cpp")]
 COPY_BYTES = 256 << 20                    # the plain copy of bench.py --pmc-probe
 M256_BYTES = 5 * 256 * 163840 * 2        # algorithmic bytes of one M=256 gather
 
 
 def kernel_source_hash() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def short_name(name: str) -> str:
