@@ -21,6 +21,7 @@ and timed per gather.
 
 Modes: default (the JSON line); ``--pmc-probe`` runs only a plain 256 MiB copy
 and the M=256 fused gather a few times, for ``rocprofv3 --pmc`` counter runs;
+``--gemm-probe`` runs only the M=256 lm_head product three times, likewise;
 ``--graph-only`` runs only the graph-replay leg (checked against the oracle),
 for a kernel trace of it.
 """
@@ -68,11 +69,13 @@ def parse_args():
     ap.add_argument("--variant", choices=["fused", "split"], default="fused")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--pmc-probe", action="store_true")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="run only the M=256 lm_head product (default implementation) three times")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the graph-replay leg of the M=1 decode gather")
     ap.add_argument("--graph-only", action="store_true",
                     help="run only the graph-replay leg (for a kernel trace of it), check it, exit")
-    ap.add_argument("--producer-steps", type=int, default=10,
+    ap.add_argument("--producer-steps", type=int, default=20,
                     help="timed M=256 lm_head producer + gather calls (0: skip)")
     return ap.parse_args()
 
@@ -136,6 +139,22 @@ def main() -> int:
             rc = push(h, ptrs, m, shi)
             return rc if rc else collect(h, m, out, shi)
         return split
+
+    if args.gemm_probe:
+        wl = syn.WORKLOADS["fused"]
+        xg = torch.randn(wl.rows, wl.hidden, device=dev).mul_(0.02).to(torch.bfloat16)
+        wg = torch.randn(wl.tp, wl.shard, wl.hidden, device=dev).mul_(0.02).to(torch.bfloat16)
+        sg = torch.empty((wl.tp, wl.rows, wl.shard), dtype=torch.bfloat16, device=dev)
+        wptrs = _lib.pointer_array([wg[r].data_ptr() for r in range(wl.tp)])
+        sptrs = _lib.pointer_array([sg[r].data_ptr() for r in range(wl.tp)])
+        for _ in range(3):
+            rc = lib.hg_lmhead(wl.tp, wl.shard, ctypes.c_void_p(xg.data_ptr()), wptrs, wl.hidden,
+                               wl.rows, sptrs, 0, sh)
+            if rc:
+                raise _lib.HgError(rc, "hg_lmhead")
+        torch.cuda.synchronize()
+        log("gemm probe done: 3 x lm_head X[256,7168] @ W[163840,7168]^T")
+        return 0
 
     # ---------------- M=256 inputs (three rotation sets) --------------------
     wl = syn.WORKLOADS["fused"]
@@ -336,23 +355,35 @@ def main() -> int:
         for _ in range(2):
             rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
             rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
-        log(f"producer timed {args.producer_steps} x (GEMM + gather) and {args.producer_steps} x GEMM")
-        with Timer(torch, stream) as t_pg:
-            for _ in range(args.producer_steps):
-                rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
-        with Timer(torch, stream) as t_lm:
-            for _ in range(args.producer_steps):
-                rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
+        # The two calls alternate, each between its own events, so that both
+        # see the same clock: under sustained MFMA load the clock drops over
+        # the first few milliseconds, and two loops run one after the other
+        # would compare a cool chip with a throttled one.
+        log(f"producer timed {args.producer_steps} x (GEMM + gather, GEMM alone), alternating")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.producer_steps)]
+        torch.cuda.synchronize()
+        for e in evs:
+            e[0].record(stream)
+            rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
+            e[1].record(stream)
+            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
+            e[2].record(stream)
+        torch.cuda.synchronize()
         if rcs:
             raise _lib.HgError(-abs(rcs), "timed producer loop")
         flops = 2.0 * wl.rows * wl.hidden * wl.vocab
         w_bytes = wl.vocab * wl.hidden * 2
-        us_pg = t_pg.ms * 1000.0 / args.producer_steps
-        us_lm = t_lm.ms * 1000.0 / args.producer_steps
+        pg = [e[0].elapsed_time(e[1]) * 1000.0 for e in evs]
+        lmt = [e[1].elapsed_time(e[2]) * 1000.0 for e in evs]
+        us_pg = statistics.median(pg)
+        us_lm = statistics.median(lmt)
         producer = {"workload": "lm_head X[256,7168] @ W[163840,7168]^T (8 ranks x 20480) BF16, "
                                 "fp32 accumulate, epilogue pushes into the mailbox, then collect",
                     "us_gemm_plus_gather": round(us_pg, 2),
                     "us_gemm_alone": round(us_lm, 2),
+                    "timing": f"median of {args.producer_steps} alternating calls, each between HIP events",
+                    "us_gemm_alone_min": round(min(lmt), 2),
                     "gemm_tflops": round(flops / (us_lm * 1e-6) / 1e12, 1),
                     "gemm_frac_of_mfma_bf16_peak": round(flops / (us_lm * 1e-6) / 2.5e15, 4),
                     "gemm_weight_gbps": round(w_bytes / (us_lm * 1e-6) / 1e9, 1),

@@ -171,6 +171,9 @@ enum GemmVariant : int {
   kGemmDirectLds64Nt = 6,  // as 5, weight loads non-temporal
   kGemmDirectLdsDeepW = 7,  // 64-wide K steps, 2 X stages + 3 weight stages, weights nt
   kGemmWave128 = 8,  // as 7 with four waves of 128 x 128 instead of eight of 128 x 64
+  kGemmTile320 = 9,  // 320 columns per workgroup, eight waves of 64 x 160, 64-wide K, 2 stages
+  kGemmTile320K32 = 10,    // as 9 with 32-wide K steps and 4 stages
+  kGemmTile320K32S3 = 11,  // as 9 with 32-wide K steps and 3 stages
 };
 // `box` (when `push`) selects the mailbox rows through a ParityArg.
 hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &shards_out, bool keep,

@@ -957,6 +957,238 @@ hipError_t launch_lmhead_w4_nt(const u32x4 *x, const ShardTable &w, const OutTab
   return launch_lmhead_w4_one<NT, false>(x, wt, ot, keep, push, box, m, hidden, shard, vocab, s);
 }
 
+// 256 x 320 output tiles: 163840 columns make 512 tiles, two full rounds on
+// 256 CUs, where 256-column tiles make 640 (three rounds, the last half
+// empty), and each K step moves 12.5 % more bytes per round trip. Eight waves
+// of 64 rows x 160 columns (2 x 5 MFMA blocks, 160 accumulator registers).
+// K step KS (64 or 32), ST LDS stages of [256 X rows + 320 weight rows]
+// (2 x 72 KB or 4 x 36 KB), loads issued ST-1 steps ahead, direct global ->
+// LDS into XOR-swizzled rows as in k_lmhead_dma. A wave's load instruction
+// fills 1024 / (2 KS) rows; the weight rows' instructions are dealt to the
+// waves in turn, so with KS = 32 (20 of them) waves 0..3 issue one more than
+// waves 4..7. Same MFMA sequence per 32 x 32 block as the other variants, so
+// the same bits.
+template <int NT, int KS, int ST, bool PUSH, bool KEEP>
+__global__ __launch_bounds__(512) void k_lmhead_n320(const u32x4 *x, ShardTableN<NT> w,
+                                                     OutTableN<NT> shards_out, ParityArg pa, int m,
+                                                     int hidden, int shard, int vocab) {
+  static_assert((KS == 64 && ST == 2) || (KS == 32 && (ST == 3 || ST == 4)), "stage plan");
+  constexpr int kTN = 320;
+  constexpr int kRowBytes = 2 * KS;
+  constexpr int kSlots = KS / 8;                  // 16-byte slots per row
+  constexpr int kRowsPerInst = 1024 / kRowBytes;  // rows one wave instruction fills
+  constexpr int kXPart = kTM * kRowBytes;
+  constexpr int kStage = (kTM + kTN) * kRowBytes;
+  constexpr int kXInst = kTM / kRowsPerInst / 8;  // per wave per step
+  constexpr int kWAll = kTN / kRowsPerInst;       // weight instructions per step
+  constexpr int kWInst = (kWAll + 7) / 8;         // most per wave
+  constexpr int kLong = kXInst + kWInst;          // loads per step, waves 0 .. kWAll%8-1
+  constexpr int kShort = kXInst + kWAll / 8;      // loads per step, the other waves
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[ST * kStage];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int mq = wave & 3;   // 64-row quarter of the tile
+  const int nh = wave >> 2;  // 160-column half of the tile
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int n0 = static_cast<int>(blockIdx.x) * kTN;
+  const int m0 = static_cast<int>(blockIdx.y) * kTM;
+  const int hv = hidden >> 3;
+  const int steps = (hidden + KS - 1) / KS;
+  const bool short_wave = kWAll % 8 != 0 && wave >= kWAll % 8;
+
+  // Instruction q of wave w fills rows kRowsPerInst*(8q+w) .. of an operand.
+  const int lrow = lane / kSlots, lslot = lane % kSlots;
+  // (arrays of the largest plan's size: with sizes that depend on the
+  // template arguments the host compiler silently drops the launch stub)
+  static_assert(kXInst <= 4 && kWInst <= 5, "per-wave load arrays");
+  const u32x4 *xsrc[4], *wsrc[5];
+  bool xok[4], wok[5];
+  int xseg[4], wseg[5];
+#pragma unroll
+  for (int q = 0; q < kXInst; ++q) {
+    const int row = kRowsPerInst * (8 * q + wave) + lrow;  // 0..255
+    xseg[q] = lslot ^ dswz<KS>(row);
+    xok[q] = m0 + row < m;
+    xsrc[q] = x + static_cast<long long>(xok[q] ? m0 + row : 0) * hv;
+  }
+#pragma unroll
+  for (int q = 0; q < kWInst; ++q) {
+    const int row = kRowsPerInst * (8 * q + wave) + lrow;  // 0..319 when 8q+w < kWAll
+    wseg[q] = lslot ^ dswz<KS>(row);
+    const int n = n0 + row;
+    const int n_wave = __builtin_amdgcn_readfirstlane(n0 + kRowsPerInst * (8 * q + wave));
+    wok[q] = 8 * q + wave < kWAll && n < vocab;
+    const int r = wok[q] ? n_wave / shard : 0;
+    wsrc[q] = w.p[r] + static_cast<long long>(wok[q] ? n - r * shard : 0) * hv;
+  }
+  // A lane whose row is out of range (or whose K segment is past `hidden`)
+  // loads from a valid address; its slot is cleared before use.
+  auto issue = [&](int kb) {
+    unsigned char *st = lds + (kb % ST) * kStage;
+#pragma unroll
+    for (int q = 0; q < kXInst; ++q) {
+      const int kv = kb * kSlots + xseg[q];
+      __builtin_amdgcn_global_load_lds(
+          xsrc[q] + (xok[q] && kv < hv ? kv : 0),
+          (__attribute__((address_space(3))) void *)(st + kRowsPerInst * (8 * q + wave) * kRowBytes),
+          16, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < kWInst; ++q) {
+      if (8 * q + wave >= kWAll) continue;  // wave-uniform
+      const int kv = kb * kSlots + wseg[q];
+      __builtin_amdgcn_global_load_lds(
+          wsrc[q] + (wok[q] && kv < hv ? kv : 0),
+          (__attribute__((address_space(3))) void *)(st + kXPart +
+                                                     kRowsPerInst * (8 * q + wave) * kRowBytes),
+          16, 0, 2 /* nt */);
+    }
+  };
+
+  f32x16 acc[2][5];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int cb = 0; cb < 5; ++cb) acc[i][cb] = f32x16{};
+
+  const bool tails = hidden % KS != 0 || m0 + kTM > m || n0 + kTN > vocab;
+  for (int p = 0; p < ST - 1 && p < steps; ++p) issue(p);
+  for (int kb = 0; kb < steps; ++kb) {
+    // Wait for this wave's loads of step kb; the later steps' stay in flight.
+    const int ahead = steps - 1 - kb < ST - 2 ? steps - 1 - kb : ST - 2;
+    if (ahead >= 2) {
+      if (short_wave) wait_vm<2 * kShort>(); else wait_vm<2 * kLong>();
+    } else if (ahead == 1) {
+      if (short_wave) wait_vm<kShort>(); else wait_vm<kLong>();
+    } else {
+      wait_vm<0>();
+    }
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+    unsigned char *sx = lds + (kb % ST) * kStage;
+    unsigned char *sw = sx + kXPart;
+    if (tails) {
+#pragma unroll
+      for (int q = 0; q < kXInst; ++q) {
+        const int kv = kb * kSlots + xseg[q];
+        if (!(xok[q] && kv < hv))
+          *reinterpret_cast<u32x4 *>(sx + (kRowsPerInst * (8 * q + wave) + lrow) * kRowBytes +
+                                     lslot * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < kWInst; ++q) {
+        const int kv = kb * kSlots + wseg[q];
+        if (8 * q + wave < kWAll && !(wok[q] && kv < hv))
+          *reinterpret_cast<u32x4 *>(sw + (kRowsPerInst * (8 * q + wave) + lrow) * kRowBytes +
+                                     lslot * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (kb + ST - 1 < steps) issue(kb + ST - 1);
+#pragma unroll
+    for (int j = 0; j < KS / 16; ++j) {
+      // K segment of this lane for MFMA j: 32-wide slice j/2, half, j%2.
+      const int g = 4 * (j >> 1) + 2 * half + (j & 1);
+      bf16x8 a[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 64 * mq + 32 * i + l32;
+        a[i] = *reinterpret_cast<const bf16x8 *>(sx + row * kRowBytes + ((g ^ dswz<KS>(row)) << 4));
+      }
+#pragma unroll
+      for (int cb = 0; cb < 5; ++cb) {
+        const int row = 160 * nh + 32 * cb + l32;
+        const bf16x8 b =
+            *reinterpret_cast<const bf16x8 *>(sw + row * kRowBytes + ((g ^ dswz<KS>(row)) << 4));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][cb], 0, 0, 0);
+      }
+    }
+  }
+
+  const bool even = (l32 & 1) == 0;
+  const int words_per_shard_row = shard >> 1;
+  const int words_per_row = vocab >> 1;
+  uint32_t *box = PUSH ? reinterpret_cast<uint32_t *>(pa.box + launch_parity(pa) * pa.stride)
+                       : nullptr;
+#pragma unroll
+  for (int cb = 0; cb < 5; ++cb) {
+    const int c0 = n0 + 160 * nh + 32 * cb;
+    if (c0 >= vocab) continue;
+    const int r = c0 / shard;
+    const int s_even = c0 - r * shard + (l32 & ~1);
+    const int wcol = s_even >> 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[t] = bf16_bits(acc[i][cb][4 * q + t]);
+        const uint32_t send = even ? (b[1] | (b[3] << 16)) : (b[0] | (b[2] << 16));
+        const uint32_t recv = swap_adjacent(send);
+        const uint32_t w0 = even ? (b[0] | (recv << 16)) : ((recv & 0xFFFFu) | (b[1] << 16));
+        const uint32_t w1 = even ? (b[2] | (recv & 0xFFFF0000u)) : ((recv >> 16) | (b[3] << 16));
+        const int rbase = m0 + 64 * mq + 32 * i + 8 * q + 4 * half;
+        const int row0 = rbase + (even ? 0 : 1);
+        const int row1 = rbase + (even ? 2 : 3);
+        if (row0 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row0) * words_per_shard_row + wcol] = w0;
+          if (PUSH)
+            box[static_cast<long long>(row0) * words_per_row + (r * shard >> 1) + wcol] =
+                w0 == kSentinel ? 0u : w0;
+        }
+        if (row1 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row1) * words_per_shard_row + wcol] = w1;
+          if (PUSH)
+            box[static_cast<long long>(row1) * words_per_row + (r * shard >> 1) + wcol] =
+                w1 == kSentinel ? 0u : w1;
+        }
+      }
+    }
+  }
+}
+
+template <int NT, int KS, int ST>
+hipError_t launch_lmhead_n320_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
+                                 bool push, const ParityArg &box, int m, int hidden, int shard,
+                                 int tp, hipStream_t s) {
+  ShardTableN<NT> wt;
+  OutTableN<NT> ot;
+  for (int r = 0; r < NT; ++r) {
+    wt.p[r] = w.p[r];
+    ot.p[r] = so.p[r];
+  }
+  const int vocab = tp * shard;
+  const dim3 grid((vocab + 319) / 320, (m + kTM - 1) / kTM);
+  if (push && keep)
+    hipLaunchKernelGGL((k_lmhead_n320<NT, KS, ST, true, true>), grid, dim3(512), 0, s, x, wt, ot,
+                       box, m, hidden, shard, vocab);
+  else if (push)
+    hipLaunchKernelGGL((k_lmhead_n320<NT, KS, ST, true, false>), grid, dim3(512), 0, s, x, wt, ot,
+                       box, m, hidden, shard, vocab);
+  else
+    hipLaunchKernelGGL((k_lmhead_n320<NT, KS, ST, false, true>), grid, dim3(512), 0, s, x, wt, ot,
+                       box, m, hidden, shard, vocab);
+  return hipGetLastError();
+}
+
+template <int KS, int ST>
+hipError_t launch_lmhead_n320(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
+                              bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
+                              hipStream_t s) {
+  if (tp <= kSmallTable)
+    return launch_lmhead_n320_nt<kSmallTable, KS, ST>(x, w, so, keep, push, box, m, hidden, shard,
+                                                      tp, s);
+  return launch_lmhead_n320_nt<HG_MAX_TP, KS, ST>(x, w, so, keep, push, box, m, hidden, shard, tp,
+                                                  s);
+}
+
 template <int NT, int KS, int ST, bool WNT>
 hipError_t launch_lmhead_dma_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
                                 bool push, const ParityArg &box, int m, int hidden, int shard,
@@ -1018,6 +1250,12 @@ hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &sh
                                                        shard, tp, s);
       return launch_lmhead_w4_nt<HG_MAX_TP>(x, w, shards_out, keep, push, box, m, hidden,
                                                    shard, tp, s);
+    case kGemmTile320:
+      return launch_lmhead_n320<64, 2>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
+    case kGemmTile320K32:
+      return launch_lmhead_n320<32, 4>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
+    case kGemmTile320K32S3:
+      return launch_lmhead_n320<32, 3>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmStaged256:
       return launch_lmhead_ncp<4>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmStaged128:

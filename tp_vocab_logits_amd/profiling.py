@@ -19,6 +19,8 @@ Usage::
     python -m tp_vocab_logits_amd.profiling kernels STATS_CSV --command CMD --out FILE.md [--trace TRACE_CSV]
     python -m tp_vocab_logits_amd.profiling counters FETCH_CSV WRITE_CSV \\
         --command-fetch CMD --command-write CMD --out FILE.json
+    python -m tp_vocab_logits_amd.profiling sq CSV [CSV ...] --kernel NAME \\
+        --command CMD [--command CMD ...] --out FILE.md
 """
 
 from __future__ import annotations
@@ -50,44 +52,68 @@ def short_name(name: str) -> str:
     return name.split("(")[0] if not name.startswith("void ") else name[5:].split("(")[0]
 
 
-def _medians(trace_csv: str | None) -> dict[str, float]:
-    """Median duration (ns) per kernel name from a ``*_kernel_trace.csv``."""
+def _dispatches(trace_csv: str | None) -> list[tuple[str, int, float]]:
+    """(kernel name, grid threads, duration ns) of every dispatch in a
+    ``*_kernel_trace.csv``."""
     if not trace_csv:
-        return {}
-    durs: dict[str, list[int]] = {}
+        return []
+    out = []
     for r in csv.DictReader(open(trace_csv)):
-        durs.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    return {k: statistics.median(v) for k, v in durs.items()}
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        out.append((r["Kernel_Name"], grid, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    return out
+
+
+def _stats(ns: list[float]) -> str:
+    return (f"{len(ns)} | {statistics.mean(ns) / 1e3:.3f} | {statistics.median(ns) / 1e3:.3f} | "
+            f"{min(ns) / 1e3:.3f} | {max(ns) / 1e3:.3f}")
 
 
 def kernels_report(stats_csv: str, command: str, trace_csv: str | None = None) -> str:
     rows = list(csv.DictReader(open(stats_csv)))
-    med = _medians(trace_csv)
+    disp = _dispatches(trace_csv)
     lines = ["# rocprofv3 kernel summary", "", "Command (TMPDIR=/tmp; paths relative to the repository root):", "",
              "    " + command, "",
-             "| kernel | calls | avg us | median us | min us | max us | share |",
-             "|---|---|---|---|---|---|---|"]
+             "Per kernel name (the `--stats` table):", "",
+             "| kernel | calls | avg us | min us | max us | share |",
+             "|---|---|---|---|---|---|"]
     for r in rows:
-        m = f"{med[r['Name']] / 1e3:.3f}" if r["Name"] in med else "-"
         lines.append(f"| `{short_name(r['Name'])}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.3f} | "
-                     f"{m} | {float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
+                     f"{float(r['MinNs'])/1e3:.3f} | {float(r['MaxNs'])/1e3:.3f} | "
                      f"{float(r['Percentage']):.1f} % |")
     lines += ["", f"Kernel source hash: `{kernel_source_hash()}`", ""]
-    # The bench runs the fused gather at M=1 (a few us per call) and at M=256
-    # (tens of us); the instantiation (vectors per lane) depends on the size.
-    for r in rows:
-        n = short_name(r["Name"])
-        if not n.startswith("hg::k_fused<"):
-            continue
-        avg = float(r["AverageNs"]) * 1e-9
-        if avg > 20e-6:
-            lines.append(f"M=256 fused gather (`{n}`): {float(r['AverageNs'])/1e3:.2f} us average -> "
-                         f"{M256_BYTES / avg / 1e9:.1f} GB/s algorithmic "
-                         f"({M256_BYTES / avg / 8e12 * 100:.1f} % of 8 TB/s).")
-        else:
-            m = f", {med[r['Name']] / 1e3:.3f} us median" if r["Name"] in med else ""
-            lines.append(f"M=1 fused gather (`{n}`): {float(r['AverageNs'])/1e3:.3f} us average "
-                         f"kernel duration{m}, {float(r['MinNs'])/1e3:.3f} us minimum.")
+    if not disp:
+        return "\n".join(lines) + "\n"
+    # One instantiation serves several row counts, so the per-name figures mix
+    # workloads; the trace separates them by launch shape (grid) and, where
+    # two row counts share a grid, by duration.
+    groups: dict[tuple[str, int], list[float]] = {}
+    for name, grid, ns in disp:
+        groups.setdefault((short_name(name), grid), []).append(ns)
+    lines += ["Per kernel and grid (from the kernel trace):", "",
+              "| kernel | grid threads | calls | avg us | median us | min us | max us |",
+              "|---|---|---|---|---|---|---|"]
+    for (n, grid), ns in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        lines.append(f"| `{n}` | {grid} | {_stats(ns)} |")
+    lines.append("")
+    fused = [(n, g, ns) for (n, g), v in groups.items() if n.startswith("hg::k_fused<") for ns in v]
+    # M=256 (about 60 us) is the only fused gather of the run above 40 us.
+    big = [ns for _, _, ns in fused if ns > 40e3]
+    if big:
+        avg = statistics.mean(big) * 1e-9
+        lines.append(f"M=256 fused gather (k_fused dispatches above 40 us): {len(big)} calls, "
+                     f"{avg * 1e6:.2f} us average, {statistics.median(big) / 1e3:.2f} us median -> "
+                     f"{M256_BYTES / avg / 1e9:.1f} GB/s algorithmic ({M256_BYTES / avg / 8e12 * 100:.1f} % of 8 TB/s).")
+    # M=1 decode: the most frequent fused launch shape (the timed loop).
+    if fused:
+        counts: dict[tuple[str, int], int] = {}
+        for n, g, _ in fused:
+            counts[(n, g)] = counts.get((n, g), 0) + 1
+        key = max(counts, key=counts.get)
+        ns = groups[key]
+        lines.append(f"M=1 decode fused gather (`{key[0]}`, grid {key[1]} threads, the most frequent fused "
+                     f"launch): {len(ns)} calls, {statistics.mean(ns) / 1e3:.3f} us average, "
+                     f"{statistics.median(ns) / 1e3:.3f} us median, {min(ns) / 1e3:.3f} us minimum.")
     return "\n".join(lines) + "\n"
 
 
@@ -131,6 +157,67 @@ def counters_report(fetch_csv: str, write_csv: str, cmd_fetch: str, cmd_write: s
     }
 
 
+# Derived quantities of the SQ report; the GPU has 8 XCDs of 32 CUs, 4 SIMDs each.
+XCDS, SIMDS = 8, 256 * 4
+
+
+def sq_report(csvs: list[str], kernel: str, commands: list[str]) -> str:
+    """Median per-dispatch SQ/TCC/GRBM counters of the kernels whose name
+    contains ``kernel``, over several ``--pmc`` runs (one counter set each)."""
+    per: dict[str, list[float]] = {}
+    durs: list[int] = []
+    clocks: list[float] = []  # GHz, GRBM_GUI_ACTIVE / 8 over the same dispatch's duration
+    names: set[str] = set()
+    for path in csvs:
+        seen: set[str] = set()
+        for r in csv.DictReader(open(path)):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            names.add(short_name(r["Kernel_Name"]))
+            per.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+            dt = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                clocks.append(float(r["Counter_Value"]) / XCDS / dt)
+            if r["Dispatch_Id"] not in seen:
+                seen.add(r["Dispatch_Id"])
+                durs.append(dt)
+    med = {k: statistics.median(v) for k, v in per.items()}
+    dur = statistics.median(durs)
+    lines = ["# SQ counters of the M=256 lm_head product (rocprofv3)", "",
+             "Kernel " + ", ".join(f"`{n}`" for n in sorted(names)) + ".", "",
+             "Commands (TMPDIR=/tmp; paths relative to the repository root):", ""]
+    lines += ["    " + c for c in commands]
+    lines += ["", f"Median over {len(durs)} profiled dispatches; median duration {dur / 1e3:.1f} us.", "",
+              "| counter | median per dispatch |", "|---|---|"]
+    lines += [f"| `{k}` | {v:.4g} |" for k, v in sorted(med.items())]
+    lines += ["", "Derived (GRBM_GUI_ACTIVE sums its 8 XCD instances):", ""]
+
+    def has(*ks):
+        return all(k in med for k in ks)
+    if has("GRBM_GUI_ACTIVE"):
+        cyc = med["GRBM_GUI_ACTIVE"] / XCDS
+        lines.append(f"- shader clock: GRBM_GUI_ACTIVE / 8 / that dispatch's duration = "
+                     f"{statistics.median(clocks):.2f} GHz (median)")
+        if has("SQ_VALU_MFMA_BUSY_CYCLES"):
+            lines.append(f"- MFMA busy per SIMD: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8)"
+                         f" = {med['SQ_VALU_MFMA_BUSY_CYCLES'] / (SIMDS * cyc) * 100:.1f} %")
+    if has("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA"):
+        lines.append(f"- busy cycles per MFMA instruction: "
+                     f"{med['SQ_VALU_MFMA_BUSY_CYCLES'] / med['SQ_INSTS_MFMA']:.1f}")
+    if has("SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE"):
+        lines.append(f"- LDS bank-conflict cycles / LDS active cycles: "
+                     f"{med['SQ_LDS_BANK_CONFLICT'] / med['SQ_LDS_IDX_ACTIVE'] * 100:.1f} %")
+    if has("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"):
+        lines.append(f"- wave time waiting on a counter (any): SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES = "
+                     f"{med['SQ_WAIT_INST_ANY'] / med['SQ_WAVE_CYCLES'] * 100:.1f} %")
+    if has("SQ_WAIT_INST_LDS", "SQ_WAVE_CYCLES"):
+        lines.append(f"- of which on LDS: SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES = "
+                     f"{med['SQ_WAIT_INST_LDS'] / med['SQ_WAVE_CYCLES'] * 100:.1f} %")
+    if has("TCC_HIT_sum", "TCC_MISS_sum"):
+        lines.append(f"- L2 hit rate: {med['TCC_HIT_sum'] / (med['TCC_HIT_sum'] + med['TCC_MISS_sum']) * 100:.1f} %")
+    return "\n".join(lines) + "\n"
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -145,8 +232,17 @@ def main() -> None:
     c.add_argument("--command-fetch", required=True)
     c.add_argument("--command-write", required=True)
     c.add_argument("--out", required=True)
+    q = sub.add_parser("sq")
+    q.add_argument("csvs", nargs="+", help="*_counter_collection.csv of each --pmc run")
+    q.add_argument("--kernel", required=True, help="substring of the kernel name")
+    q.add_argument("--command", action="append", required=True)
+    q.add_argument("--out", required=True)
     a = ap.parse_args()
-    if a.what == "kernels":
+    if a.what == "sq":
+        text = sq_report(a.csvs, a.kernel, a.command)
+        open(a.out, "w").write(text)
+        print(text)
+    elif a.what == "kernels":
         text = kernels_report(a.stats_csv, a.command, a.trace)
         open(a.out, "w").write(text)
         print(text)
