@@ -252,6 +252,24 @@ def test_stock_gather_kernel():
         assert np.array_equal(bits(out), og.stock_concat(list(s)))
 
 
+@pytest.mark.parametrize("dtype,width", [(torch.float32, 4), (torch.float32, 12), (torch.int8, 48),
+                                         (torch.float64, 2), (torch.float16, 24), (torch.float32, 3)])
+def test_stock_gather_moves_bytes_of_any_dtype(dtype, width):
+    # rows of a multiple of 16 bytes run in the library kernel, the rest in torch.cat;
+    # both give the rank-order concatenation, byte for byte
+    note(f"stock gather dtype={dtype} width={width}")
+    tp, m = 3, 5
+    g = torch.Generator().manual_seed(width)
+    raw = torch.randint(0, 256, (tp, m, width * torch.empty((), dtype=dtype).element_size()),
+                        dtype=torch.uint8, generator=g)
+    shards = raw.view(dtype).to(DEV)
+    out = stock_gather(shards, tp)
+    want = np.concatenate([raw[r].numpy() for r in range(tp)], axis=1)
+    assert np.array_equal(out.cpu().view(torch.uint8).numpy(), want)
+    with pytest.raises(ValueError):
+        stock_gather(shards.cpu(), tp)
+
+
 def test_graph_capture_declines_to_stock():
     tp, shard, cap = 2, 2048, 1
     note("graph capture decline")

@@ -57,20 +57,28 @@ def stock_gather(shards: torch.Tensor | Sequence[torch.Tensor], tp: int,
                  out: torch.Tensor | None = None) -> torch.Tensor:
     """The stock gather: rank-order concatenation ``[M, TP*S]``, bytes
     unchanged (the single-device share of an all-gather followed by the copy to
-    ``[M, V]``). BF16 shards with ``S % 8 == 0`` run in the library's kernel;
-    other dtypes or widths fall to ``torch.cat`` on the shards' device."""
+    ``[M, V]``). The shards must be on a CUDA device. Rows of a multiple of 16
+    bytes (any dtype: the concatenation only moves bytes) run in the library's
+    kernel; other widths take ``torch.cat`` on the device."""
     ptrs, m, s, device, dtype = _shard_pointers(shards, tp)
+    if device.type != "cuda":
+        raise ValueError(f"shards must be on a CUDA device, got {device}")
     if out is None:
         out = torch.empty((m, tp * s), dtype=dtype, device=device)
-    if dtype != torch.bfloat16 or s % 8 or device.type != "cuda":
+    elif out.dtype != dtype or tuple(out.shape) != (m, tp * s) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {dtype} [{m}, {tp * s}] tensor")
+    row_bytes = s * torch.empty((), dtype=dtype).element_size()
+    if row_bytes % 16:
         parts = list(shards) if not isinstance(shards, torch.Tensor) else list(shards.unbind(0))
         torch.cat(parts, dim=1, out=out)
         return out
     if m == 0:
         return out
     with torch.cuda.device(device):
-        check(lib().hg_stock_gather(tp, s, pointer_array(ptrs), m, ctypes.c_void_p(out.data_ptr()),
-                                    _stream_handle(device)), "hg_stock_gather")
+        # the kernel counts the row in BF16 elements (two bytes each)
+        check(lib().hg_stock_gather(tp, row_bytes // 2, pointer_array(ptrs), m,
+                                    ctypes.c_void_p(out.data_ptr()), _stream_handle(device)),
+              "hg_stock_gather")
     return out
 
 
