@@ -1,5 +1,6 @@
-"""Build libhg.so (the HIP kernels and the C ABI) in-tree for gfx950, and the
-``_hgcall`` extension (fast-call Python wrappers of the per-call entry points).
+"""Build libhg.so (the HIP kernels and the C ABI) in-tree for gfx950, the
+``_hgcall`` extension (fast-call Python wrappers of the per-call entry points)
+and ``tests/c_client/hg_client`` (a plain C client of the ABI).
 
 Usage: ``python -m tp_vocab_logits_amd.build`` (or ``__graft_entry__.build()``).
 Always recompiles; each result replaces the previous file atomically.
@@ -22,6 +23,9 @@ LIB = os.path.join(PKG, "libhg.so")
 SOURCES = ["hg_api.cpp", "hg_kernels.hip", "hg_lmhead.hip"]
 ARCH = "gfx950"
 FASTCALL = os.path.join(PKG, "_hgcall" + sysconfig.get_config_var("EXT_SUFFIX"))
+C_CLIENT_DIR = os.path.join(ROOT, "tests", "c_client")
+C_CLIENT = os.path.join(C_CLIENT_DIR, "hg_client")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 
 
 def hipcc() -> str:
@@ -63,9 +67,34 @@ def build_fastcall(verbose: bool = False) -> str:
     return FASTCALL
 
 
+def build_c_client(verbose: bool = False) -> str:
+    """Compile the plain C client of the ABI (tests/c_client/hg_client.c, host
+    code only, linked against libhg.so and the HIP runtime) and return its
+    path. Needs libhg.so to exist."""
+    fd, tmp = tempfile.mkstemp(prefix="hg_client.", suffix=".tmp", dir=C_CLIENT_DIR)
+    os.close(fd)
+    try:
+        cmd = [os.environ.get("CC", "gcc"), "-O2", "-std=c11", "-Wall", "-Wextra",
+               "-D__HIP_PLATFORM_AMD__", "-I", INCLUDE, "-I", os.path.join(ROCM, "include"),
+               os.path.join(C_CLIENT_DIR, "hg_client.c"), "-o", tmp,
+               "-L", PKG, "-l:libhg.so", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+               "-Wl,-rpath,$ORIGIN/../../tp_vocab_logits_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("hg_client build failed:\n" + (res.stderr or res.stdout))
+        os.chmod(tmp, 0o755)
+        os.replace(tmp, C_CLIENT)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return C_CLIENT
+
+
 def build(verbose: bool = False) -> str:
-    """Compile libhg.so and the _hgcall extension; return libhg.so's path.
-    Raises on a compiler error."""
+    """Compile libhg.so, the _hgcall extension and the C client; return
+    libhg.so's path. Raises on a compiler error."""
     build_fastcall(verbose)
     fd, tmp = tempfile.mkstemp(prefix="libhg.", suffix=".so.tmp", dir=PKG)
     os.close(fd)
@@ -85,6 +114,7 @@ def build(verbose: bool = False) -> str:
     finally:
         if os.path.exists(tmp):
             os.unlink(tmp)
+    build_c_client(verbose)
     return LIB
 
 
