@@ -17,7 +17,8 @@ mailbox poll read, output write, re-arm write).
 
 The JSON line also carries ``decode_graph``: the same K decode gathers
 captured into one HIP graph, with the parity kept in device memory, replayed
-and timed per gather.
+and timed per gather; and ``decode_split``: the same gathers through the split
+variant (push, then collect).
 
 Modes: default (the JSON line); ``--pmc-probe`` runs only a plain 256 MiB copy
 and the M=256 fused gather a few times, for ``rocprofv3 --pmc`` counter runs;
@@ -253,6 +254,24 @@ def main() -> int:
     if args.variant == "fused" and args.graph:
         us_graph, hg_g, g_outs = graph_leg()
 
+    # ---------------- decode, split variant: push + collect per gather ------
+    us_split = None
+    if args.variant == "fused":
+        hg_s = HeadGather(wd.tp, wd.shard, wd.cap, device=dev)
+        s_outs = torch.empty((n_out, wd.rows, wd.vocab), dtype=torch.bfloat16, device=dev)
+        s_addr = [s_outs[n].data_ptr() for n in range(n_out)]
+        fs = call_fn(hg_s, "split")
+        for n in range(args.warmup):
+            if fs(dec_addr[n % wd.pool], wd.rows, s_addr[n % n_out]):
+                raise _lib.HgError(-1, "split warmup")
+        log(f"decode timed {args.steps} split gathers (push + collect)")
+        with Timer(torch, stream) as t_split:
+            for n in range(args.steps):
+                rcs |= fs(dec_addr[n % wd.pool], wd.rows, s_addr[n])
+        if rcs:
+            raise _lib.HgError(-abs(rcs), "timed split loop")
+        us_split = t_split.ms * 1000.0 / args.steps
+
     # ---------------- M=256 gather: cold (rotating) and back-to-back -------
     fn_big = call_fn(hg_big, args.variant)
     for n in range(6):
@@ -412,6 +431,14 @@ def main() -> int:
         if hg_g.parity != 0 or hg_g.poll_status() != _lib.HG_OK:  # 2 replays of K calls: even
             log("FAIL: device parity after the graph replays")
             return 1
+    if us_split is not None:
+        for p in (0, 1):
+            if not torch.equal(hg_s.mailbox(p).view(torch.int32), armed):
+                log("FAIL: split decode mailbox not all-sentinel")
+                return 1
+        if hg_s.poll_status() != _lib.HG_OK:
+            log("FAIL: a bounded poll of the split variant gave up")
+            return 1
     if hg.poll_status() != _lib.HG_OK or hg_big.poll_status() != _lib.HG_OK:
         log("FAIL: a bounded poll gave up")
         return 1
@@ -472,6 +499,12 @@ def main() -> int:
                 if not np.array_equal(got[k], want_dec[k]):
                     log(f"FAIL: graph-replayed decode output of call {k} differs from the oracle")
                     return 1
+        if us_split is not None:
+            got = s_outs[: wd.pool].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            for k in range(min(wd.pool, args.steps)):
+                if not np.array_equal(got[k], want_dec[k]):
+                    log(f"FAIL: split decode output of call {k} differs from the oracle")
+                    return 1
         if not np.array_equal(syn.from_torch_bf16(big_out[0]), want_big):
             log("FAIL: M=256 output differs from the oracle")
             return 1
@@ -527,6 +560,10 @@ def main() -> int:
             "workload": "the same M=1 decode gathers captured into one HIP graph "
                         "(device-side parity) and replayed",
             "us_per_gather": round(us_graph, 3), "gathers_per_replay": args.steps},
+        "decode_split": None if us_split is None else {
+            "workload": "the same M=1 decode gathers through the split variant "
+                        "(hg_push then hg_collect: two launches per gather)",
+            "us_per_gather": round(us_split, 3)},
         "large_m": {"workload": "gather TP=8, V=163840, M=256, cap=256, 3 rotating buffer sets",
                     "us_per_gather_cold": round(us_cold, 3),
                     "gbps_algorithmic_cold": round(gbps_cold, 1),
