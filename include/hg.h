@@ -31,8 +31,9 @@
  *    stated otherwise.
  *  - Every device pointer must be 16-byte aligned and belong to the context's
  *    device, which must be the current device at the call (else HG_EINVAL).
- *  - Ownership: the context owns its mailbox and a 256-byte status block;
- *    the caller owns every shard, output and weight buffer.
+ *  - Ownership: the context owns its mailbox and a status block of 65792
+ *    bytes (the poll-timeout counter and 16384 device parity slots); the
+ *    caller owns every shard, output and weight buffer.
  *  - Ordering: all calls on one context are issued from one host thread at a
  *    time, on one stream, in call order. Two uses of one parity are then
  *    separated by a use of the other, and a push into a parity starts only
@@ -144,6 +145,8 @@ int hg_collect(hg_ctx *h, int m, void *out, void *stream);
  * all-gather into [TP, M, V/TP] followed by a copy to [M, V]): rank-order
  * concatenation into out[m][tp*shard], every byte unchanged (no sentinel
  * rewrite). Needs no context; tp in [1, HG_MAX_TP], shard % 8 == 0, m >= 0.
+ * Only bytes move, so shards of another element type can pass their row
+ * width in 2-byte units (row bytes / 2) as `shard`.
  */
 int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *out, void *stream);
 
