@@ -116,3 +116,15 @@ def test_fastcall_binding():
         f.gather(0, 0, 1, 0)
     with pytest.raises(OverflowError):
         f.collect(0, 1 << 40, 0, 0)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no fallback implementation: without libhg.so the loader raises (every
+    # entry point of the binding goes through it)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libhg.so"))
+    monkeypatch.setattr(_lib, "_LIB", None)
+    monkeypatch.setattr(_lib, "_FAST", None)
+    with pytest.raises(ImportError):
+        _lib.lib()
+    with pytest.raises(ImportError):
+        _lib.fast()
