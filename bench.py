@@ -290,6 +290,31 @@ def main() -> int:
     gbps_cold = big_bytes / (us_cold * 1e-6) / 1e9
     gbps_hot = big_bytes / (us_hot * 1e-6) / 1e9
 
+    # ---------------- the same bytes through a plain streaming kernel -------
+    # (read the shards, write mailbox-sized rows, read rows back, write an
+    # output, re-arm the rows; no compare, no poll), on the same rotating
+    # shard sets, cold: the practical ceiling of this read/write mix here
+    ref = _lib.ref()
+    props = torch.cuda.get_device_properties(dev)
+    row_vectors = wl.rows * wl.vocab * 2 // 16
+    ref_boxes = [torch.empty(wl.rows * wl.vocab, dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    ref_outs = [torch.empty(wl.rows * wl.vocab, dtype=torch.bfloat16, device=dev) for _ in range(3)]
+
+    def ref_call(n):
+        return ref.hgref_stream(big_dev[n % 3].data_ptr(), ref_boxes[n % 2].data_ptr(),
+                                ref_boxes[(n + 1) % 2].data_ptr(), ref_outs[n % 3].data_ptr(),
+                                row_vectors, 4 * props.multi_processor_count, sh)
+    for n in range(6):
+        rcs |= ref_call(n)
+    log(f"M=256 plain streaming reference, {args.large_steps} calls, 3 rotating sets")
+    with Timer(torch, stream) as t_ref:
+        for n in range(args.large_steps):
+            rcs |= ref_call(n)
+    if rcs:
+        raise _lib.HgError(-abs(rcs), "reference streaming loop")
+    us_ref = t_ref.ms * 1000.0 / args.large_steps
+    del ref_boxes, ref_outs
+
     # ---------------- the other workloads: tiny, spec (M=4), batched (M=64) --
     # back-to-back eager calls on their own input pools; outputs of each pool
     # set are checked in the cpu_baseline leg
@@ -567,6 +592,11 @@ def main() -> int:
         "large_m": {"workload": "gather TP=8, V=163840, M=256, cap=256, 3 rotating buffer sets",
                     "us_per_gather_cold": round(us_cold, 3),
                     "gbps_algorithmic_cold": round(gbps_cold, 1),
+                    "us_plain_stream_same_bytes_cold": round(us_ref, 3),
+                    "plain_stream_over_gather": round(us_ref / us_cold, 4),
+                    "plain_stream": "hgref_stream (libhgref.so): the same 5 x M x V x 2 bytes "
+                                    "with 128-bit accesses and no compare or poll, 4 workgroups "
+                                    "of 256 per CU, same rotating shard sets",
                     "us_per_gather_back_to_back": round(us_hot, 3),
                     "gbps_algorithmic_back_to_back": round(gbps_hot, 1),
                     "algorithmic_bytes_per_gather": big_bytes},

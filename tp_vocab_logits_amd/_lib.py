@@ -101,6 +101,26 @@ def lib() -> ctypes.CDLL:
     return _LIB
 
 
+_REF = None
+
+
+def ref() -> ctypes.CDLL:
+    """libhgref.so: the reference streaming kernel the benchmark times beside
+    the gather (``hgref_stream``). Raises if it was not built."""
+    global _REF
+    if _REF is None:
+        path = os.path.join(os.path.dirname(LIB_PATH), "libhgref.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it with `python -m tp_vocab_logits_amd.build`")
+        handle = ctypes.CDLL(path)
+        handle.hgref_stream.restype = ctypes.c_int
+        handle.hgref_stream.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_void_p, ctypes.c_longlong, ctypes.c_int,
+                                        ctypes.c_void_p]
+        _REF = handle
+    return _REF
+
+
 _FAST = None
 
 

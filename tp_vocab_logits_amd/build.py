@@ -23,6 +23,7 @@ LIB = os.path.join(PKG, "libhg.so")
 SOURCES = ["hg_api.cpp", "hg_kernels.hip", "hg_lmhead.hip"]
 ARCH = "gfx950"
 FASTCALL = os.path.join(PKG, "_hgcall" + sysconfig.get_config_var("EXT_SUFFIX"))
+REF_LIB = os.path.join(PKG, "libhgref.so")  # the benchmark's reference streaming kernel
 C_CLIENT_DIR = os.path.join(ROOT, "tests", "c_client")
 C_CLIENT = os.path.join(C_CLIENT_DIR, "hg_client")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
@@ -60,6 +61,7 @@ def build_fastcall(verbose: bool = False) -> str:
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError("_hgcall build failed:\n" + (res.stderr or res.stdout))
+        os.chmod(tmp, 0o755)
         os.replace(tmp, FASTCALL)
     finally:
         if os.path.exists(tmp):
@@ -92,6 +94,28 @@ def build_c_client(verbose: bool = False) -> str:
     return C_CLIENT
 
 
+def build_ref(verbose: bool = False) -> str:
+    """Compile libhgref.so: the reference streaming kernel bench.py times beside
+    the gather (hg_stream_ref.hip; not part of libhg.so's ABI)."""
+    fd, tmp = tempfile.mkstemp(prefix="libhgref.", suffix=".so.tmp", dir=PKG)
+    os.close(fd)
+    try:
+        cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+               "-fvisibility=hidden", "-Wall",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-x", "hip", os.path.join(CSRC, "hg_stream_ref.hip"), "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError("libhgref.so build failed:\n" + (res.stderr or res.stdout))
+        os.replace(tmp, REF_LIB)
+    finally:
+        if os.path.exists(tmp):
+            os.unlink(tmp)
+    return REF_LIB
+
+
 def build(verbose: bool = False) -> str:
     """Compile libhg.so, the _hgcall extension and the C client; return
     libhg.so's path. Raises on a compiler error."""
@@ -115,6 +139,7 @@ def build(verbose: bool = False) -> str:
         if os.path.exists(tmp):
             os.unlink(tmp)
     build_c_client(verbose)
+    build_ref(verbose)
     return LIB
 
 
