@@ -156,7 +156,7 @@ OPS = [("fused", 6), ("declined", 2), ("split", 3), ("partial", 3), ("producer",
        ("vocab_change", 2), ("mode_switch", 2), ("graph", 2), ("arm", 1)]
 
 
-@pytest.mark.parametrize("seed", [1, 2, 3, 4, 5, 6, 7, 8])
+@pytest.mark.parametrize("seed", list(range(1, 33)))
 def test_random_mixed_sequence(seed):
     run = Run(seed)
     names = [n for n, wgt in OPS for _ in range(wgt)]
