@@ -165,7 +165,7 @@ int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *o
  * HG_EINVAL unless 1 <= tp <= HG_MAX_TP, shard >= 32 and shard % 32 == 0,
  * hidden >= 8 and hidden % 8 == 0, m >= 0, pointers non-NULL and 16-byte
  * aligned. m == 0 does nothing. The result is deterministic (no split-K).
- * variant: the implementation -- 0 the default (9); 1 256 output columns per
+ * variant: the implementation -- 0 the default (12); 1 256 output columns per
  * workgroup with direct global-to-LDS loads, 32-wide K steps, 4 stages; 2
  * 256 columns with loads staged through registers; 3 128 columns staged
  * through registers; 4 as 1 with non-temporal weight loads; 5 as 1 with
@@ -174,7 +174,9 @@ int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *o
  * 8 as 7 with four waves per workgroup, each computing 128 x 128 outputs; 9
  * 320 output columns per workgroup (eight waves of 64 x 160), 64-wide K
  * steps, 2 stages of each operand; 10 as 9 with 32-wide K steps and 4
- * stages; 11 as 10 with 3 stages.
+ * stages; 11 as 10 with 3 stages; 12 as 9 with buffer loads into LDS (the
+ * global-address form makes the compiler wait for every LDS read at each
+ * MFMA group).
  * Every variant performs the same sequence of fp32 MFMA accumulations and
  * gives the same bits.
  */

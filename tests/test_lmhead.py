@@ -82,7 +82,7 @@ def test_hand_worked_golden_product():
     assert np.all(out[0, :, 4:] == 0)
 
 
-VARIANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11]
+VARIANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)

@@ -67,10 +67,10 @@ struct Tuning {
 };
 
 constexpr int kGridPerCu = 4;
-constexpr int kDefaultGemmVariant = hg::kGemmTile320;
+constexpr int kDefaultGemmVariant = hg::kGemmTile320Buf;
 
 bool valid_gemm_variant(int v) {
-  return v >= 0 && v <= hg::kGemmTile320K32S3;
+  return v >= 0 && v <= hg::kGemmTile320Buf;
 }
 
 bool valid_block(int b) { return b == 64 || b == 128 || b == 256 || b == 512 || b == 1024; }

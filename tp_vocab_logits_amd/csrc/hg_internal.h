@@ -174,6 +174,7 @@ enum GemmVariant : int {
   kGemmTile320 = 9,  // 320 columns per workgroup, eight waves of 64 x 160, 64-wide K, 2 stages
   kGemmTile320K32 = 10,    // as 9 with 32-wide K steps and 4 stages
   kGemmTile320K32S3 = 11,  // as 9 with 32-wide K steps and 3 stages
+  kGemmTile320Buf = 12,    // as 9 with buffer loads into LDS
 };
 // `box` (when `push`) selects the mailbox rows through a ParityArg.
 hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &shards_out, bool keep,

@@ -1182,6 +1182,235 @@ hipError_t launch_lmhead_n320_nt(const u32x4 *x, const ShardTable &w, const OutT
   return hipGetLastError();
 }
 
+// As k_lmhead_n320 with 64-wide K steps and 2 stages, but the loads are
+// buffer loads into LDS (buffer_load_dwordx4 ... lds), as in k_lmhead_w4:
+// with the global-address form the compiler waits for every outstanding LDS
+// read at each MFMA group, so each pair of MFMAs sits out a whole LDS round
+// trip. X: one resource from the tile's first row. Weights: with ONE_RANK
+// (shard a multiple of 320, so no tile straddles two ranks) one resource from
+// the tile's first row; otherwise one per load instruction, from the first of
+// its 8 rows (all of one rank, as shard % 32 == 0).
+template <int NT, bool ONE_RANK, bool PUSH, bool KEEP>
+__global__ __launch_bounds__(512) void k_lmhead_n320b(const u32x4 *x, ShardTableN<NT> w,
+                                                      OutTableN<NT> shards_out, ParityArg pa,
+                                                      int m, int hidden, int shard, int vocab) {
+  constexpr int KS = 64;
+  constexpr int kTN = 320;
+  constexpr int kRowBytes = 128;
+  constexpr int kSlots = 8;
+  constexpr int kXPart = kTM * kRowBytes;           // 32 KB
+  constexpr int kStage = (kTM + kTN) * kRowBytes;   // 72 KB
+  constexpr int kXInst = 4, kWInst = 5;             // per wave per step
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
+
+  const int tid = static_cast<int>(threadIdx.x);
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int mq = wave & 3;   // 64-row quarter of the tile
+  const int nh = wave >> 2;  // 160-column half of the tile
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+  const int n0 = static_cast<int>(blockIdx.x) * kTN;
+  const int m0 = static_cast<int>(blockIdx.y) * kTM;
+  const int hv = hidden >> 3;
+  const int steps = (hidden + KS - 1) / KS;
+
+  // Instruction q of wave w fills rows 8*(8q+w) .. +8 of an operand. A lane
+  // whose row is out of range (or whose K segment is past `hidden`) loads
+  // offset 0 instead; its slot is cleared before use.
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const int xrows = m - m0 < kTM ? m - m0 : kTM;
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<u32x4 *>(x + static_cast<long long>(m0) * hv), 0, xrows * hidden * 2,
+      kRawBufferWord3);
+  __amdgpu_buffer_rsrc_t wres[kWInst];
+  int xoff[kXInst], woff[kWInst], xseg[kXInst], wseg[kWInst];
+  bool xok[kXInst], wok[kWInst];
+#pragma unroll
+  for (int q = 0; q < kXInst; ++q) {
+    const int row = 8 * (8 * q + wave) + lrow;  // 0..255
+    xseg[q] = lslot ^ dswz<64>(row);
+    xok[q] = row < xrows;
+    xoff[q] = row * hv * 16;
+  }
+  if constexpr (ONE_RANK) {
+    const int r = n0 / shard;
+    const int trows = vocab - n0 < kTN ? vocab - n0 : kTN;
+    wres[0] = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<u32x4 *>(w.p[r] + static_cast<long long>(n0 - r * shard) * hv), 0,
+        trows * hidden * 2, kRawBufferWord3);
+  }
+#pragma unroll
+  for (int q = 0; q < kWInst; ++q) {
+    const int row = 8 * (8 * q + wave) + lrow;  // 0..319
+    wseg[q] = lslot ^ dswz<64>(row);
+    wok[q] = n0 + row < vocab;
+    if constexpr (ONE_RANK) {
+      woff[q] = row * hv * 16;
+    } else {
+      const int nfirst = __builtin_amdgcn_readfirstlane(n0 + 8 * (8 * q + wave));
+      const int r = nfirst < vocab ? nfirst / shard : 0;
+      const int s0 = nfirst < vocab ? nfirst - r * shard : 0;
+      const int grows = nfirst < vocab ? (vocab - nfirst < 8 ? vocab - nfirst : 8) : 1;
+      wres[q] = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<u32x4 *>(w.p[r] + static_cast<long long>(s0) * hv), 0, grows * hidden * 2,
+          kRawBufferWord3);
+      woff[q] = lrow * hv * 16;
+    }
+  }
+  auto issue = [&](int kb) {
+    unsigned char *st = lds + (kb & 1) * kStage;
+#pragma unroll
+    for (int q = 0; q < kXInst; ++q) {
+      const int kv = kb * kSlots + xseg[q];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void *)(st + 8 * (8 * q + wave) * kRowBytes),
+          16, xok[q] && kv < hv ? xoff[q] + kv * 16 : 0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < kWInst; ++q) {
+      const int kv = kb * kSlots + wseg[q];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wres[ONE_RANK ? 0 : q],
+          (__attribute__((address_space(3))) void *)(st + kXPart + 8 * (8 * q + wave) * kRowBytes),
+          16, wok[q] && kv < hv ? woff[q] + kv * 16 : 0, 0, 0, kPolicyNt);
+    }
+  };
+
+  f32x16 acc[2][5];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int cb = 0; cb < 5; ++cb) acc[i][cb] = f32x16{};
+
+  const bool tails = hidden % KS != 0 || m0 + kTM > m || n0 + kTN > vocab;
+  issue(0);
+  for (int kb = 0; kb < steps; ++kb) {
+    wait_vm<0>();  // this wave's loads of step kb (nothing newer is in flight)
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    __asm__ __volatile__("" ::: "memory");
+    unsigned char *sx = lds + (kb & 1) * kStage;
+    unsigned char *sw = sx + kXPart;
+    if (tails) {
+#pragma unroll
+      for (int q = 0; q < kXInst; ++q) {
+        const int kv = kb * kSlots + xseg[q];
+        if (!(xok[q] && kv < hv))
+          *reinterpret_cast<u32x4 *>(sx + (8 * (8 * q + wave) + lrow) * kRowBytes + lslot * 16) =
+              u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int q = 0; q < kWInst; ++q) {
+        const int kv = kb * kSlots + wseg[q];
+        if (!(wok[q] && kv < hv))
+          *reinterpret_cast<u32x4 *>(sw + (8 * (8 * q + wave) + lrow) * kRowBytes + lslot * 16) =
+              u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    if (kb + 1 < steps) issue(kb + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // K segment of this lane for MFMA j: 32-wide slice j/2, half, j%2.
+      const int g = 4 * (j >> 1) + 2 * half + (j & 1);
+      bf16x8 a[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = 64 * mq + 32 * i + l32;
+        a[i] = *reinterpret_cast<const bf16x8 *>(sx + row * kRowBytes + ((g ^ dswz<64>(row)) << 4));
+      }
+#pragma unroll
+      for (int cb = 0; cb < 5; ++cb) {
+        const int row = 160 * nh + 32 * cb + l32;
+        const bf16x8 b =
+            *reinterpret_cast<const bf16x8 *>(sw + row * kRowBytes + ((g ^ dswz<64>(row)) << 4));
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][cb], 0, 0, 0);
+      }
+    }
+  }
+
+  const bool even = (l32 & 1) == 0;
+  const int words_per_shard_row = shard >> 1;
+  const int words_per_row = vocab >> 1;
+  uint32_t *box = PUSH ? reinterpret_cast<uint32_t *>(pa.box + launch_parity(pa) * pa.stride)
+                       : nullptr;
+#pragma unroll
+  for (int cb = 0; cb < 5; ++cb) {
+    const int c0 = n0 + 160 * nh + 32 * cb;
+    if (c0 >= vocab) continue;
+    const int r = c0 / shard;
+    const int s_even = c0 - r * shard + (l32 & ~1);
+    const int wcol = s_even >> 1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t b[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) b[t] = bf16_bits(acc[i][cb][4 * q + t]);
+        const uint32_t send = even ? (b[1] | (b[3] << 16)) : (b[0] | (b[2] << 16));
+        const uint32_t recv = swap_adjacent(send);
+        const uint32_t w0 = even ? (b[0] | (recv << 16)) : ((recv & 0xFFFFu) | (b[1] << 16));
+        const uint32_t w1 = even ? (b[2] | (recv & 0xFFFF0000u)) : ((recv >> 16) | (b[3] << 16));
+        const int rbase = m0 + 64 * mq + 32 * i + 8 * q + 4 * half;
+        const int row0 = rbase + (even ? 0 : 1);
+        const int row1 = rbase + (even ? 2 : 3);
+        if (row0 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row0) * words_per_shard_row + wcol] = w0;
+          if (PUSH)
+            box[static_cast<long long>(row0) * words_per_row + (r * shard >> 1) + wcol] =
+                w0 == kSentinel ? 0u : w0;
+        }
+        if (row1 < m) {
+          if (KEEP) shards_out.p[r][static_cast<long long>(row1) * words_per_shard_row + wcol] = w1;
+          if (PUSH)
+            box[static_cast<long long>(row1) * words_per_row + (r * shard >> 1) + wcol] =
+                w1 == kSentinel ? 0u : w1;
+        }
+      }
+    }
+  }
+}
+
+template <int NT, bool ONE_RANK>
+hipError_t launch_lmhead_n320b_one(const u32x4 *x, const ShardTableN<NT> &wt,
+                                   const OutTableN<NT> &ot, bool keep, bool push,
+                                   const ParityArg &box, int m, int hidden, int shard, int vocab,
+                                   hipStream_t s) {
+  const dim3 grid((vocab + 319) / 320, (m + kTM - 1) / kTM);
+  if (push && keep)
+    hipLaunchKernelGGL((k_lmhead_n320b<NT, ONE_RANK, true, true>), grid, dim3(512), 0, s, x, wt,
+                       ot, box, m, hidden, shard, vocab);
+  else if (push)
+    hipLaunchKernelGGL((k_lmhead_n320b<NT, ONE_RANK, true, false>), grid, dim3(512), 0, s, x, wt,
+                       ot, box, m, hidden, shard, vocab);
+  else
+    hipLaunchKernelGGL((k_lmhead_n320b<NT, ONE_RANK, false, true>), grid, dim3(512), 0, s, x, wt,
+                       ot, box, m, hidden, shard, vocab);
+  return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_lmhead_n320b_nt(const u32x4 *x, const ShardTable &w, const OutTable &so,
+                                  bool keep, bool push, const ParityArg &box, int m, int hidden,
+                                  int shard, int tp, hipStream_t s) {
+  ShardTableN<NT> wt;
+  OutTableN<NT> ot;
+  for (int r = 0; r < NT; ++r) {
+    wt.p[r] = w.p[r];
+    ot.p[r] = so.p[r];
+  }
+  const int vocab = tp * shard;
+  if (shard % 320 == 0)
+    return launch_lmhead_n320b_one<NT, true>(x, wt, ot, keep, push, box, m, hidden, shard, vocab,
+                                             s);
+  return launch_lmhead_n320b_one<NT, false>(x, wt, ot, keep, push, box, m, hidden, shard, vocab,
+                                            s);
+}
+
 template <int KS, int ST>
 hipError_t launch_lmhead_n320(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
                               bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
@@ -1260,6 +1489,12 @@ hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &sh
       return launch_lmhead_n320<32, 4>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmTile320K32S3:
       return launch_lmhead_n320<32, 3>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
+    case kGemmTile320Buf:
+      if (tp <= kSmallTable)
+        return launch_lmhead_n320b_nt<kSmallTable>(x, w, shards_out, keep, push, box, m, hidden,
+                                                   shard, tp, s);
+      return launch_lmhead_n320b_nt<HG_MAX_TP>(x, w, shards_out, keep, push, box, m, hidden,
+                                               shard, tp, s);
     case kGemmStaged256:
       return launch_lmhead_ncp<4>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
     case kGemmStaged128:
