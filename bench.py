@@ -422,6 +422,22 @@ def main() -> int:
         lmt = [e[1].elapsed_time(e[2]) * 1000.0 for e in evs]
         us_pg = statistics.median(pg)
         us_lm = statistics.median(lmt)
+        # the same product for one decode row (M=1, rows 1..255 of X unused):
+        # a weight stream; alternating again, medians
+        evs1 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                for _ in range(args.producer_steps)]
+        torch.cuda.synchronize()
+        for e in evs1:
+            e[0].record(stream)
+            rcs |= gg(h, xptr, wptrs, wl.hidden, 1, optr, None, sh)
+            e[1].record(stream)
+            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, 1, sptrs, 0, sh)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        if rcs:
+            raise _lib.HgError(-abs(rcs), "timed M=1 producer loop")
+        us_pg1 = statistics.median(e[0].elapsed_time(e[1]) * 1000.0 for e in evs1)
+        us_lm1 = statistics.median(e[1].elapsed_time(e[2]) * 1000.0 for e in evs1)
         producer = {"workload": "lm_head X[256,7168] @ W[163840,7168]^T (8 ranks x 20480) BF16, "
                                 "fp32 accumulate, epilogue pushes into the mailbox, then collect",
                     "us_gemm_plus_gather": round(us_pg, 2),
@@ -431,7 +447,9 @@ def main() -> int:
                     "gemm_tflops": round(flops / (us_lm * 1e-6) / 1e12, 1),
                     "gemm_frac_of_mfma_bf16_peak": round(flops / (us_lm * 1e-6) / 2.5e15, 4),
                     "gemm_weight_gbps": round(w_bytes / (us_lm * 1e-6) / 1e9, 1),
-                    "gemm_weight_frac_of_hbm_peak": round(w_bytes / (us_lm * 1e-6) / 8e12, 4)}
+                    "gemm_weight_frac_of_hbm_peak": round(w_bytes / (us_lm * 1e-6) / 8e12, 4),
+                    "m1": {"us_gemm_plus_gather": round(us_pg1, 2), "us_gemm_alone": round(us_lm1, 2),
+                           "gemm_weight_gbps": round(w_bytes / (us_lm1 * 1e-6) / 1e9, 1)}}
         # the gather of the producer path against the oracle applied to the product's own shards
         rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
         rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)

@@ -176,7 +176,7 @@ int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *o
  * steps, 2 stages of each operand; 10 as 9 with 32-wide K steps and 4
  * stages; 11 as 10 with 3 stages; 12 as 9 with buffer loads into LDS (the
  * global-address form makes the compiler wait for every LDS read at each
- * MFMA group).
+ * MFMA group), whose waves with no row below m only load.
  * Every variant performs the same sequence of fp32 MFMA accumulations and
  * gives the same bits.
  */

@@ -1258,10 +1258,17 @@ __global__ __launch_bounds__(512) void k_lmhead_n320b(const u32x4 *x, ShardTable
       woff[q] = lrow * hv * 16;
     }
   }
+  // X load instructions whose 8 rows all lie past m are not issued: rows past
+  // m only ever reach output rows that are not stored, so their LDS slots may
+  // hold anything (likewise weight rows past the vocabulary).
+  bool xinst[kXInst];
+#pragma unroll
+  for (int q = 0; q < kXInst; ++q) xinst[q] = 8 * (8 * q + wave) < xrows;  // wave-uniform
   auto issue = [&](int kb) {
     unsigned char *st = lds + (kb & 1) * kStage;
 #pragma unroll
     for (int q = 0; q < kXInst; ++q) {
+      if (!xinst[q]) continue;
       const int kv = kb * kSlots + xseg[q];
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           xres, (__attribute__((address_space(3))) void *)(st + 8 * (8 * q + wave) * kRowBytes),
@@ -1283,7 +1290,12 @@ __global__ __launch_bounds__(512) void k_lmhead_n320b(const u32x4 *x, ShardTable
 #pragma unroll
     for (int cb = 0; cb < 5; ++cb) acc[i][cb] = f32x16{};
 
-  const bool tails = hidden % KS != 0 || m0 + kTM > m || n0 + kTN > vocab;
+  // Only a K segment past `hidden` must read as zero: it meets real data in
+  // the other operand. Such slots (loaded from offset 0) are cleared.
+  const bool ktail = hidden % KS != 0;
+  // A wave whose 64 rows all lie at or past m computes nothing (wave-uniform):
+  // at small m most waves only stream loads.
+  const bool blk0 = m0 + 64 * mq < m;
   issue(0);
   for (int kb = 0; kb < steps; ++kb) {
     wait_vm<0>();  // this wave's loads of step kb (nothing newer is in flight)
@@ -1292,24 +1304,25 @@ __global__ __launch_bounds__(512) void k_lmhead_n320b(const u32x4 *x, ShardTable
     __asm__ __volatile__("" ::: "memory");
     unsigned char *sx = lds + (kb & 1) * kStage;
     unsigned char *sw = sx + kXPart;
-    if (tails) {
+    if (ktail && (kb + 1) * kSlots > hv) {
 #pragma unroll
       for (int q = 0; q < kXInst; ++q) {
         const int kv = kb * kSlots + xseg[q];
-        if (!(xok[q] && kv < hv))
+        if (xinst[q] && kv >= hv)
           *reinterpret_cast<u32x4 *>(sx + (8 * (8 * q + wave) + lrow) * kRowBytes + lslot * 16) =
               u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int q = 0; q < kWInst; ++q) {
         const int kv = kb * kSlots + wseg[q];
-        if (!(wok[q] && kv < hv))
+        if (kv >= hv)
           *reinterpret_cast<u32x4 *>(sw + (8 * (8 * q + wave) + lrow) * kRowBytes + lslot * 16) =
               u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
     }
     if (kb + 1 < steps) issue(kb + 1);
+    if (!blk0) continue;  // no row of this wave's 64 below m: loads only
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       // K segment of this lane for MFMA j: 32-wide slice j/2, half, j%2.
