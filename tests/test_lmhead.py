@@ -168,3 +168,35 @@ def test_producer_gather_declines_and_state():
     status, want = sim.gather(list(bits(shards)))
     assert status == og.OK and np.array_equal(bits(out), want) and hg.parity == sim.parity
     hg.close()
+
+
+@pytest.mark.parametrize("m", [1, 5, 40])
+def test_producer_gather_every_variant_knob(m):
+    # hg_gemm_gather with each implementation chosen through the tuning knob:
+    # the same shards (bit for bit) and the gather of them, parity alternating
+    tp, shard, hidden, cap = 3, 96, 136, 64
+    note(f"producer variants m={m}")
+    x = dev(rand_bits((m, hidden), 0.5, 70 + m))
+    w = dev(rand_bits((tp, shard, hidden), 0.5, 80 + m))
+    hg = HeadGather(tp, shard, cap, device=DEV)
+    hg.set_poll_limit(1 << 20)
+    sim = og.MailboxSim(tp, shard, cap)
+    ref = None
+    for variant in [0] + VARIANTS:
+        hg.set_tuning(_lib.TUNE_GEMM_VARIANT, variant)
+        shards = torch.empty((tp, m, shard), dtype=torch.bfloat16, device=DEV)
+        out = hg.gemm_gather(x, w, shards_out=shards)
+        if ref is None:
+            ref = shards.clone()
+        assert torch.equal(shards.view(torch.int16), ref.view(torch.int16)), variant
+        status, want = sim.gather(list(bits(shards)))
+        assert status == og.OK and np.array_equal(bits(out), want), variant
+        assert hg.parity == sim.parity
+    assert hg.poll_status() == _lib.HG_OK
+    for p in (0, 1):
+        assert np.array_equal(bits(hg.mailbox(p)), sim.mailbox_bf16(p))
+    with pytest.raises(HgError):
+        hg.set_tuning(_lib.TUNE_GEMM_VARIANT, max(VARIANTS) + 1)
+    with pytest.raises(HgError):
+        hg.set_tuning(_lib.TUNE_GEMM_VARIANT, -1)
+    hg.close()
