@@ -153,6 +153,22 @@ def test_fused_launch_shapes(block, push, poll, grid, skew):
     run_lockstep(hg, sim, sets, 6, "fused")
 
 
+@pytest.mark.parametrize("block", [64, 128, 512, 1024])
+@pytest.mark.parametrize("vpt", [1, 2, 4])
+def test_split_launch_shapes(block, vpt):
+    """The split variant's push and collect kernels at every block size and
+    vectors per lane, on a ragged geometry (36 vectors per shard row)."""
+    note(f"split shapes block={block} vpt={vpt}")
+    tp, shard, cap = 3, 288, 4
+    hg = make(tp, shard, cap, split_block=block, split_vpt=vpt)
+    sim = og.MailboxSim(tp, shard, cap)
+    w = syn.WORKLOADS["spec"]
+    sets = [syn.shard_set(w, k, rows=m, tp=tp, shard=shard) for k, m in enumerate([4, 1, 3, 2])]
+    for s in sets:
+        syn.inject_sentinel_words(s, 0.05, 11 + s.shape[1])
+    run_lockstep(hg, sim, sets, 6, "split")
+
+
 def test_decode_1000_back_to_back():
     w = syn.WORKLOADS["decode"]
     note(f"decode tp={w.tp} V={w.vocab} m={w.rows} cap={w.cap} calls={w.calls}")
