@@ -31,7 +31,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import os
 import statistics
@@ -43,9 +42,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "µs per logits gather at M=1 (V=163840, TP=8) + achieved HBM GB/s at M=256"
 HBM_PEAK_GBPS = 8000.0
-# the sources that fix the gather kernels and their launch shapes
-KERNEL_SOURCES = [os.path.join(ROOT, "tp_vocab_logits_amd", "csrc", f)
-                  for f in ("hg_kernels.hip", "hg_internal.h", "hg_api.cpp")]
 COUNTERS = os.path.join(ROOT, "profiles", "fused_gather_m256_counters.json")
 
 
@@ -54,11 +50,11 @@ def log(msg: str) -> None:
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the sources that fix the gather kernels and their launch shapes
+    (the one the counter summary in profiles/ records)."""
+    from tp_vocab_logits_amd.profiling import kernel_source_hash as h
+
+    return h()
 
 
 def parse_args():
