@@ -223,7 +223,8 @@ int hg_set_device_parity(hg_ctx *h, int enable, void *stream);
  * The mailbox protocol is unchanged -- every word is pushed, polled and
  * re-armed. vocab = tp*shard (the default) writes whole rows; vocab % 8 == 0
  * keeps 16-byte stores, other widths store element by element. HG_EINVAL
- * unless 1 <= vocab <= tp*shard. Calls already enqueued keep their width.
+ * unless 1 <= vocab <= tp*shard. Calls already enqueued keep their width,
+ * and so do calls captured into a graph, on every replay.
  */
 int hg_set_vocab(hg_ctx *h, int vocab);
 
