@@ -196,3 +196,35 @@ def test_full_size_slices(name, vocab):
         assert_guard(flat, w.rows, vocab)
     assert_state(hg, sim)
     hg.close()
+
+
+def test_graph_keeps_its_captured_width_after_set_vocab():
+    # a call captured at one width replays at that width after the context's
+    # vocabulary changed; eager calls take the new width; the parity keeps
+    # alternating across both
+    tp, shard, cap, m = 3, 264, 2, 2
+    v_cap, v_new = 3 * 264 - 9, 530
+    note(f"graph width {v_cap} kept after set_vocab({v_new})")
+    hg, sim = HeadGather(tp, shard, cap, device=DEV, vocab=v_cap), og.MailboxSim(tp, shard, cap)
+    hg.set_poll_limit(1 << 20)
+    hg.set_device_parity(True)
+    static_in = dev(inputs(tp, shard, m, 400))
+    flat, static_out = guarded_out(m, v_cap)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        hg(static_in, out=static_out)
+    hg.set_vocab(v_new)
+    for rep in range(3):
+        s = inputs(tp, shard, m, 410 + rep)
+        static_in.copy_(dev(s))
+        g.replay()
+        torch.cuda.synchronize()
+        status, want = sim.gather(list(s))
+        assert status == og.OK
+        assert np.array_equal(bits(static_out), og.slice_vocab(want, v_cap)), rep
+        assert_guard(flat, m, v_cap)
+        e = inputs(tp, shard, 1, 420 + rep)
+        got = hg(dev(e))
+        status, want = sim.gather(list(e))
+        assert status == og.OK and np.array_equal(bits(got), og.slice_vocab(want, v_new)), rep
+    assert_state(hg, sim)
