@@ -11,7 +11,15 @@
 // custom all-gather for TP logits" (Test Result) has the gather overlap the
 // tail of this GEMM; here the GEMM's epilogue performs the push itself.
 //
-// Work decomposition: a workgroup of 2*NCP waves owns a 256-row x 64*NCP
+// Variants (selected by the `variant` argument): the default is
+// k_lmhead_n320b -- 256 x 320 output tiles, eight waves of 64 x 160,
+// buffer loads straight into LDS, and at small M the waves with no row below
+// M only load. The others below are the measured alternatives, kept
+// selectable: register-staged loads (k_lmhead), direct loads into LDS with
+// 256 columns (k_lmhead_dma, k_lmhead_dma2), four waves of 128 x 128
+// (k_lmhead_w4) and 320 columns with the global-address loads (k_lmhead_n320).
+//
+// Work decomposition of the first: a workgroup of 2*NCP waves owns a 256-row x 64*NCP
 // column output tile (all of M = 256 at once); wave w computes rows
 // 128*(w%2) .. +128 and columns 64*(w/2) .. +64 as 4 x 2 blocks of
 // v_mfma_f32_32x32x16_bf16. Per 64-wide K step both operand tiles -- X
