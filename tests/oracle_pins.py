@@ -18,6 +18,7 @@ Independent sources used here, never the oracle itself:
 
 from __future__ import annotations
 
+import itertools
 import os
 
 import numpy as np
@@ -300,9 +301,65 @@ def check_vocab_slice(g) -> None:
         raise AssertionError(f"vocab {bad} accepted")
 
 
+# The call kinds of the exhaustive sequences: (name, rows, how). `cap` is 2.
+SEQ_OPS = [("gather", 1, "fused"), ("gather", 2, "fused"), ("decline", 0, "fused"),
+           ("decline", 3, "fused"), ("decline", 1, "capture"), ("split", 1, "split"),
+           ("split", 2, "split"), ("split", 1, "ranks"), ("arm", 0, "arm")]
+
+
+def check_protocol_sequences(g) -> None:
+    """Every sequence of three calls from SEQ_OPS on TP=2, S=8, cap=2, each on
+    fresh random data with forced sentinel pairs: a served call gives the
+    definition, a declined one the unrewritten concat; the parity is the
+    number of served calls since the last arm, mod 2; after a push exactly
+    rows 0..m-1 of the current parity hold the rewritten words; after every
+    call the whole mailbox is the sentinel again."""
+    tp, s, cap = 2, 8, 2
+    sent = torch_sentinel()
+    rng = np.random.default_rng(31)
+    for seq in itertools.product(range(len(SEQ_OPS)), repeat=3):
+        sim = g.MailboxSim(tp, s, cap)
+        served = 0
+        for k in seq:
+            kind, m, how = SEQ_OPS[k]
+            if how == "arm":
+                sim.arm()
+                served = 0
+            else:
+                shards = rand_bits(rng, (tp, m, s))
+                if m > 0:
+                    force_pairs(shards, rng, min(2, tp * m * s // 2))
+                want = g.gather_definition(list(shards)) if m > 0 else None
+                if how == "fused":
+                    status, out = sim.gather(list(shards))
+                elif how == "capture":
+                    status, out = sim.gather(list(shards), capturing=True)
+                else:
+                    if how == "split":
+                        assert sim.push(list(shards)) == g.OK
+                    else:
+                        assert sim.push_ranks(list(shards), [1]) == g.OK
+                        assert sim.push_ranks(list(shards), [0]) == g.OK
+                    box = sim.box.copy()
+                    assert np.array_equal(box[served % 2, :m], torch_words(want))
+                    assert np.all(box[served % 2, m:] == sent)
+                    assert np.all(box[1 - served % 2] == sent)
+                    status, out = sim.collect(m)
+                if kind == "decline":
+                    assert status == g.DECLINE, seq
+                    assert np.array_equal(out, np.concatenate(list(shards), axis=1)), seq
+                else:
+                    assert status == g.OK, seq
+                    assert np.array_equal(out, want), seq
+                    served += 1
+            assert sim.parity == served % 2, seq
+            assert np.all(sim.box == sent), seq
+
+
 GATHER_CHECKS = [check_sentinel_constant, check_packing, check_golden_gather, check_layout_nccl,
                  check_value_equivalence_and_xor, check_exhaustive_tiny, check_protocol,
-                 check_partial_push, check_create_rules, check_vocab_slice]
+                 check_protocol_sequences, check_partial_push, check_create_rules,
+                 check_vocab_slice]
 
 
 # ---------------------------------------------------------------------------
