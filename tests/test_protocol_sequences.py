@@ -2,7 +2,8 @@
 protocol simulator -- fused gathers at 1 and cap rows, declines (no rows, too
 many rows, host parity under graph capture), split push + collect, a push by
 the two ranks separately, and re-arm -- with outputs, parity and both mailbox
-parities compared after each sequence. TP=2, S=16, cap=2."""
+parities compared after each sequence, with the parity kept on the host and
+on the device. TP=2, S=16, cap=2."""
 
 from __future__ import annotations
 
@@ -34,11 +35,15 @@ def dev(b: np.ndarray) -> torch.Tensor:
     return syn.to_torch_bf16(b, DEV)
 
 
+@pytest.mark.parametrize("device_parity", [False, True], ids=["host-parity", "device-parity"])
 @pytest.mark.parametrize("first", range(len(OPS)), ids=[f"{o[0]}{o[1]}-{o[2]}" for o in OPS])
-def test_all_three_call_sequences(first):
-    print(f"[gpu] sequences starting with {OPS[first]}", flush=True)
+def test_all_three_call_sequences(first, device_parity):
+    """With the parity on the host a captured call declines (stock result,
+    parity kept); with device-side parity it is served on replay."""
+    print(f"[gpu] sequences starting with {OPS[first]}, device parity {device_parity}", flush=True)
     hg = HeadGather(TP, SHARD, CAP, device=DEV)
     hg.set_poll_limit(1 << 20)
+    hg.set_device_parity(device_parity)
     k = 0
     for rest in itertools.product(range(len(OPS)), repeat=2):
         seq = (first,) + rest
@@ -65,7 +70,7 @@ def test_all_three_call_sequences(first):
                 g.replay()
                 torch.cuda.synchronize()
                 got = out
-                status, want = sim.gather(list(s), capturing=True)
+                status, want = sim.gather(list(s), capturing=not device_parity)
             elif how == "split":
                 assert hg.push(dev(s)) and sim.push(list(s)) == og.OK
                 got = hg.collect(m)
@@ -76,7 +81,8 @@ def test_all_three_call_sequences(first):
                 assert hg.push_ranks(d, [0]) and sim.push_ranks(list(s), [0]) == og.OK
                 got = hg.collect(m)
                 status, want = sim.collect(m)
-            assert status == (og.DECLINE if kind == "decline" else og.OK), seq
+            served = kind != "decline" or (how == "capture" and device_parity)
+            assert status == (og.OK if served else og.DECLINE), seq
             assert np.array_equal(bits(got), want), (seq, i)
         assert hg.parity == sim.parity, seq
         for p in (0, 1):
