@@ -24,8 +24,19 @@ Contents:
 * :mod:`oracle.gemm` -- the vocab-parallel lm_head shard product in float64
   and a float -> BF16 round-to-nearest-even written from the IEEE-754 format.
 
-Every function here is pinned by ``tests/test_oracle_*.py`` against facts the
-pages or mathematics fix; none is "parity unpinned".
+Pins (``tests/oracle_pins.py``, run by ``tests/test_oracle_pins.py``; each
+planted mistake of ``tests/test_oracle_mutants.py`` trips at least one):
+
+* the gather definition, the protocol simulator, the vocabulary slice and the
+  construction rules: torch's BF16 memory layout, numpy's stack/transpose for
+  the NCCL layout, a hand-worked golden gather, an exhaustive 4^8 tiny case,
+  value equivalence and an XOR invariant, randomised call sequences;
+* ``lm_head_shard`` / ``lm_head_entry``: a hand-worked golden product, one-hot
+  and closed-form inputs, torch's float64 matmul;
+* ``round_to_bf16`` / ``bf16_to_f64``: torch's float32 -> BF16 conversion over
+  every class of float32 input;
+* ``relative_frobenius_error``: hand-worked norm ratios
+  (``tests/golden/rel_frobenius_error.txt``).
 """
 
 from . import gather, gemm  # noqa: F401

@@ -445,5 +445,25 @@ def check_bf16_rounding(gm) -> None:
     assert np.all((got[nan] & 0x7FFF) > 0x7F80)
 
 
+def check_rel_frobenius_golden(gm) -> None:
+    """The relative Frobenius error against the hand-worked cases of
+    ``tests/golden/rel_frobenius_error.txt`` (exact ratios of norms worked out
+    by hand), and its symmetry under a common sign flip."""
+    gd = read_golden("rel_frobenius_error.txt")
+    shapes = {r[0]: (int(r[1]), int(r[2])) for r in gd["shape"]}
+    exact = {r[0]: np.array([float(v) for v in r[1:]]).reshape(shapes[r[0]]) for r in gd["exact"]}
+    approx = {r[0]: np.array([int(v, 16) for v in r[1:]], np.uint16).reshape(shapes[r[0]])
+              for r in gd["approx"]}
+    want = {r[0]: int(r[1]) / int(r[2]) for r in gd["err"]}
+    assert set(want) == set(exact) == set(approx)
+    for case, w in want.items():
+        got = gm.relative_frobenius_error(approx[case], exact[case])
+        assert abs(got - w) <= 1e-15 * max(w, 1.0), (case, got, w)
+        # -A against -E: the same distance over the same norm
+        neg = approx[case] ^ np.uint16(0x8000)
+        got = gm.relative_frobenius_error(neg, -exact[case])
+        assert abs(got - w) <= 1e-15 * max(w, 1.0), (case, "negated", got, w)
+
+
 GEMM_CHECKS = [check_gemm_golden, check_gemm_one_hot, check_gemm_closed_forms, check_gemm_library,
-               check_bf16_rounding]
+               check_bf16_rounding, check_rel_frobenius_golden]

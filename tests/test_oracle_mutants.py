@@ -167,6 +167,24 @@ def _bf16_to_f64_wrong_shift(bits):
     return (b.astype(np.uint32) << np.uint32(15)).view(np.float32).astype(np.float64)
 
 
+def _rel_err_squared(approx_bits, exact):
+    approx = gemm.bf16_to_f64(approx_bits)
+    exact = np.asarray(exact, dtype=np.float64)
+    return float(np.sum((approx - exact) ** 2) / np.sum(exact ** 2))
+
+
+def _rel_err_over_approx(approx_bits, exact):
+    approx = gemm.bf16_to_f64(approx_bits)
+    exact = np.asarray(exact, dtype=np.float64)
+    return float(np.linalg.norm(approx - exact) / np.linalg.norm(approx))
+
+
+def _rel_err_max_abs(approx_bits, exact):
+    approx = gemm.bf16_to_f64(approx_bits)
+    exact = np.asarray(exact, dtype=np.float64)
+    return float(np.max(np.abs(approx - exact)) / np.max(np.abs(exact)))
+
+
 def _slice_tail(out, vocab):
     out = np.asarray(out, np.uint16)
     return out[:, out.shape[1] - vocab:].copy()
@@ -211,6 +229,10 @@ MUTANTS = [
     ("bf16 rounding truncates", gemm, {"round_to_bf16": _round_truncate}),
     ("bf16 rounding ties away", gemm, {"round_to_bf16": _round_ties_away}),
     ("bf16 decode shifted wrong", gemm, {"bf16_to_f64": _bf16_to_f64_wrong_shift}),
+    ("relative error squared", gemm, {"relative_frobenius_error": _rel_err_squared}),
+    ("relative error over the approximation's norm", gemm,
+     {"relative_frobenius_error": _rel_err_over_approx}),
+    ("relative error as a max-norm ratio", gemm, {"relative_frobenius_error": _rel_err_max_abs}),
 ]
 
 
