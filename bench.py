@@ -146,7 +146,7 @@ def main() -> int:
         sptrs = _lib.pointer_array([sg[r].data_ptr() for r in range(wl.tp)])
         for _ in range(3):
             rc = lib.hg_lmhead(wl.tp, wl.shard, ctypes.c_void_p(xg.data_ptr()), wptrs, wl.hidden,
-                               wl.rows, sptrs, 0, sh)
+                               wl.rows, sptrs, sh)
             if rc:
                 raise _lib.HgError(rc, "hg_lmhead")
         torch.cuda.synchronize()
@@ -350,15 +350,17 @@ def main() -> int:
     s_big = [torch.empty((wl.rows, wl.vocab), dtype=torch.bfloat16, device=dev) for _ in range(3)]
     s_big_p = [o.data_ptr() for o in s_big]
     for n in range(args.warmup):
-        rcs |= stock_fn(wd.tp, wd.shard, dec_addr[n % wd.pool], wd.rows, s_small_p[n % wd.pool], shi)
+        rcs |= stock_fn(wd.tp, wd.shard, dec_addr[n % wd.pool], wd.rows, s_small_p[n % wd.pool],
+                        wd.vocab, shi)
     with Timer(torch, stream) as t_sd:
         for n in range(args.steps):
-            rcs |= stock_fn(wd.tp, wd.shard, dec_addr[n % wd.pool], wd.rows, s_small_p[n % wd.pool], shi)
+            rcs |= stock_fn(wd.tp, wd.shard, dec_addr[n % wd.pool], wd.rows, s_small_p[n % wd.pool],
+                        wd.vocab, shi)
     for n in range(3):
-        rcs |= stock_fn(wl.tp, wl.shard, big_addr[n], wl.rows, s_big_p[n], shi)
+        rcs |= stock_fn(wl.tp, wl.shard, big_addr[n], wl.rows, s_big_p[n], wl.vocab, shi)
     with Timer(torch, stream) as t_sb:
         for n in range(args.large_steps):
-            rcs |= stock_fn(wl.tp, wl.shard, big_addr[n % 3], wl.rows, s_big_p[n % 3], shi)
+            rcs |= stock_fn(wl.tp, wl.shard, big_addr[n % 3], wl.rows, s_big_p[n % 3], wl.vocab, shi)
     if rcs:
         raise _lib.HgError(-abs(rcs), "stock gather loop")
     us_stock_m1 = t_sd.ms * 1000.0 / args.steps
@@ -394,7 +396,7 @@ def main() -> int:
         h = hg_big.handle
         for _ in range(2):
             rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
-            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
+            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, sh)
         # The two calls alternate, each between its own events, so that both
         # see the same clock: under sustained MFMA load the clock drops over
         # the first few milliseconds, and two loops run one after the other
@@ -407,7 +409,7 @@ def main() -> int:
             e[0].record(stream)
             rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
             e[1].record(stream)
-            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
+            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, sh)
             e[2].record(stream)
         torch.cuda.synchronize()
         if rcs:
@@ -427,7 +429,7 @@ def main() -> int:
             e[0].record(stream)
             rcs |= gg(h, xptr, wptrs, wl.hidden, 1, optr, None, sh)
             e[1].record(stream)
-            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, 1, sptrs, 0, sh)
+            rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, 1, sptrs, sh)
             e[2].record(stream)
         torch.cuda.synchronize()
         if rcs:
@@ -447,7 +449,7 @@ def main() -> int:
                     "m1": {"us_gemm_plus_gather": round(us_pg1, 2), "us_gemm_alone": round(us_lm1, 2),
                            "gemm_weight_gbps": round(w_bytes / (us_lm1 * 1e-6) / 1e9, 1)}}
         # the gather of the producer path against the oracle applied to the product's own shards
-        rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, 0, sh)
+        rcs |= lm(wl.tp, wl.shard, xptr, wptrs, wl.hidden, wl.rows, sptrs, sh)
         rcs |= gg(h, xptr, wptrs, wl.hidden, wl.rows, optr, None, sh)
         torch.cuda.synchronize()
         del w_dev

@@ -29,17 +29,19 @@
  *  - `stream` is a hipStream_t passed as void* (NULL: the null stream). Device
  *    work is enqueued on it and the call returns without waiting, unless
  *    stated otherwise.
- *  - Every device pointer must be 16-byte aligned and belong to the context's
- *    device, which must be the current device at the call (else HG_EINVAL).
+ *  - Every device pointer must be 16-byte aligned (unless stated otherwise)
+ *    and belong to the context's device, which must be the current device at
+ *    the call (else HG_EINVAL).
  *  - Ownership: the context owns its mailbox and a status block of 65792
  *    bytes (the poll-timeout counter and 16384 device parity slots); the
  *    caller owns every shard, output and weight buffer.
- *  - Ordering: all calls on one context are issued from one host thread at a
- *    time, on one stream, in call order. Two uses of one parity are then
- *    separated by a use of the other, and a push into a parity starts only
- *    after the previous kernel on it finished re-arming (API page, HeadGather
- *    class description). This is documented, not enforced: calls on different
- *    streams can race.
+ *  - Ordering: the library relies on the caller to issue every call on a
+ *    context from one host thread at a time and on a single stream, in the
+ *    order the calls are made. Stream order is what keeps a kernel from
+ *    pushing into mailbox rows that an earlier kernel is still polling or
+ *    re-arming; the library does not check it, so calls on two streams, or
+ *    two contexts sharing buffers, can race (the pages state the same
+ *    one-stream assumption: API page, HeadGather class description).
  */
 #ifndef HG_H
 #define HG_H
@@ -80,11 +82,17 @@ typedef struct hg_ctx hg_ctx;
 int hg_create(int tp, int shard, int cap, hg_ctx **out);
 
 /* Free the mailbox and the context. NULL-safe. Synchronises the device first
- * so no enqueued kernel still uses the mailbox. */
+ * so no enqueued kernel still uses the mailbox. The pages show no teardown of
+ * the mailbox object (API page, HeadGather.__init__ source allocates it for
+ * the life of the gather object); this is its end of life. */
 int hg_destroy(hg_ctx *h);
 
 /* Re-arm both parities to all-sentinel, reset the parity to 0 and drop any
- * pending split push (stream-ordered on `stream`). Recovery after an error. */
+ * pending split push (stream-ordered on `stream`). Recovery after an error.
+ * The pages arm the mailbox only when it is built (API page, HeadGather
+ * class description and HeadGather.__init__ source: a fresh mailbox is armed
+ * and the parity starts at 0); re-arming later and resetting the parity with
+ * it is our reading, so that an armed mailbox always starts at parity 0. */
 int hg_arm(hg_ctx *h, void *stream);
 
 /*
@@ -111,22 +119,32 @@ int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, void *stre
 
 /*
  * Split variant, first half: push the shards into the current parity's rows
- * 0..m-1 (sentinel words rewritten) and leave the call pending. Same
- * arguments, declines and errors as hg_gather; HG_ESTATE if a push is already
- * pending. The parity does not change.
+ * 0..m-1 (sentinel words rewritten) and leave the call pending. This is the
+ * push half of the one-shot kernel (API page, module description: each rank
+ * writes its shard into row m of the mailbox at its column offset, with the
+ * sentinel pair sent as (+0, +0)), launched on its own. Same arguments,
+ * declines and errors as hg_gather; HG_ESTATE if a push is already pending
+ * (the pages have no split call; refusing a second push before the collect
+ * is our reading, as a pending call owns its parity's rows). The parity does
+ * not change.
  */
 int hg_push(hg_ctx *h, const void *const *shards, int m, void *stream);
 
 /*
  * Split variant, partial push: only the ranks whose bit is set in `ranks`
  * (bit r = rank r) push their fragments; shards[r] is read only for those.
- * Each rank of a real TP group pushes its own fragment on its own schedule;
- * this entry point lets virtual ranks do the same. Pushes of disjoint rank
- * sets with the same m accumulate into one pending call. HG_ESTATE if a rank
- * already pushed into the pending call or m differs from it; HG_EINVAL if
- * `ranks` is empty or names a rank >= tp. A collect issued while some rank
- * has not pushed polls words that never arrive: its bounded poll gives up
- * (see hg_set_poll_limit / hg_poll_status).
+ * Each rank of a real TP group pushes its own fragment on its own schedule
+ * (API page, module description: every rank pushes into every peer's mailbox
+ * and the consumer polls until all fragments have landed); this entry point
+ * lets virtual ranks do the same. The pages do not show pushes of separate
+ * rank sets; accumulating them into one pending call, and letting a collect
+ * with a rank missing give up through the bounded poll, is our reading.
+ * Pushes of disjoint rank sets with the same m accumulate into one pending
+ * call. HG_ESTATE if a rank already pushed into the pending call or m
+ * differs from it; HG_EINVAL if `ranks` is empty or names a rank >= tp. A
+ * collect issued while some rank has not pushed polls words that never
+ * arrive: its bounded poll gives up (see hg_set_poll_limit /
+ * hg_poll_status).
  */
 int hg_push_ranks(hg_ctx *h, const void *const *shards, int m, unsigned long long ranks,
                   void *stream);
@@ -134,21 +152,32 @@ int hg_push_ranks(hg_ctx *h, const void *const *shards, int m, unsigned long lon
 /*
  * Split variant, second half: poll rows 0..m-1 of the pending parity until no
  * word is the sentinel, copy them to `out` ([m][vocab] BF16, as for
- * hg_gather) and re-arm them; then flip the parity. HG_ESTATE unless a push
- * of the same m is pending (from any set of ranks); HG_EDECLINE (nothing
- * changes) if the stream is capturing while the parity is kept on the host.
+ * hg_gather) and re-arm them; then flip the parity (API page, module
+ * description: poll, copy, re-arm; HeadGather.__call__ source: the parity
+ * flips once per served call). HG_ESTATE unless a push of the same m is
+ * pending (from any set of ranks; not on the pages -- a collect with nothing
+ * pushed would only poll until it gives up, so it is refused up front);
+ * HG_EDECLINE (nothing changes) if the stream is capturing while the parity
+ * is kept on the host.
  */
 int hg_collect(hg_ctx *h, int m, void *out, void *stream);
 
 /*
  * The stock gather's single-device share (API page, module description: the
- * all-gather into [TP, M, V/TP] followed by a copy to [M, V]): rank-order
- * concatenation into out[m][tp*shard], every byte unchanged (no sentinel
- * rewrite). Needs no context; tp in [1, HG_MAX_TP], shard % 8 == 0, m >= 0.
- * Only bytes move, so shards of another element type can pass their row
- * width in 2-byte units (row bytes / 2) as `shard`.
+ * all-gather into [TP, M, V/TP] followed by a copy to [M, V]) with the
+ * padded-vocab slice applied (PR page, Purpose: the gathered logits keep the
+ * real vocabulary's columns): rank-order concatenation, every byte unchanged
+ * (no sentinel rewrite), of which the first `vocab` columns of each row are
+ * written to out[m][vocab]. Needs no context; tp in [1, HG_MAX_TP],
+ * shard >= 1, 1 <= vocab <= tp*shard, m >= 0 (m == 0 does nothing). With
+ * shard % 8 == 0 the shards and `out` must be 16-byte aligned and rows move
+ * in 16-byte vectors; other widths move element by element and need 2-byte
+ * alignment. Only bytes move, so shards of another element type can pass
+ * their row width and `vocab` in 2-byte units (bytes / 2). HG_EINVAL on a
+ * bad size, a NULL or misaligned pointer, or a shard overlapping `out`.
  */
-int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *out, void *stream);
+int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *out, int vocab,
+                    void *stream);
 
 /*
  * The lm_head shard product that feeds the gather (API page, module
@@ -164,39 +193,33 @@ int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *o
  *             BF16, row-major; must not overlap x or w.
  * HG_EINVAL unless 1 <= tp <= HG_MAX_TP, shard >= 32 and shard % 32 == 0,
  * hidden >= 8 and hidden % 8 == 0, m >= 0, pointers non-NULL and 16-byte
- * aligned. m == 0 does nothing. The result is deterministic (no split-K).
- * variant: the implementation -- 0 the default (12); 1 256 output columns per
- * workgroup with direct global-to-LDS loads, 32-wide K steps, 4 stages; 2
- * 256 columns with loads staged through registers; 3 128 columns staged
- * through registers; 4 as 1 with non-temporal weight loads; 5 as 1 with
- * 64-wide K steps and 2 stages; 6 as 5 with non-temporal weight loads; 7
- * 64-wide K steps with 2 X stages and 3 weight stages (all 160 KB of LDS);
- * 8 as 7 with four waves per workgroup, each computing 128 x 128 outputs; 9
- * 320 output columns per workgroup (eight waves of 64 x 160), 64-wide K
- * steps, 2 stages of each operand; 10 as 9 with 32-wide K steps and 4
- * stages; 11 as 10 with 3 stages; 12 as 9 with buffer loads into LDS (the
- * global-address form makes the compiler wait for every LDS read at each
- * MFMA group), whose waves with no row below m only load.
- * Every variant performs the same sequence of fp32 MFMA accumulations and
- * gives the same bits.
+ * aligned. m == 0 does nothing. The result is deterministic (no split-K):
+ * each output is one fixed chain of fp32 accumulations over the hidden
+ * dimension, so repeated calls, and hg_gemm_gather, give the same bits.
  */
 int hg_lmhead(int tp, int shard, const void *x, const void *const *w, int hidden, int m,
-              void *const *shards_out, int variant, void *stream);
+              void *const *shards_out, void *stream);
 
 /*
  * Producer and gather: the lm_head product above whose epilogue pushes its
  * words -- sentinel rewritten -- straight into rows 0..m-1 of the current
  * parity (no shard round trip), then the collect kernel polls, copies to
- * `out` ([m][tp*shard] BF16) and re-arms; the parity flips. Two launches on
- * `stream`. When shards_out is non-NULL the product's BF16 shards are also
- * written there, bytes as computed. Declines, state errors and pointer rules
- * as hg_gather; the size rules of hg_lmhead also apply (HG_EINVAL).
+ * `out` ([m][vocab] BF16, vocab as set by hg_set_vocab) and re-arms; the
+ * parity flips. Two launches on `stream`. The PR page (Test Result) has the
+ * one-shot gather launched early enough to overlap the tail of the LM-head
+ * GEMM; here the GEMM's own epilogue is the push. When shards_out is
+ * non-NULL the product's BF16 shards are also written there, bytes as
+ * computed. Declines and state errors as hg_gather; the size rules of
+ * hg_lmhead also apply. HG_EINVAL when `out`, the mailbox, x, any weight
+ * block or any shards_out block overlap one another.
  */
 int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hidden, int m, void *out,
                    void *const *shards_out, void *stream);
 
-/* The parity the next served call will use (0 or 1), or HG_EINVAL. With
- * device-side parity on, this synchronises the device and reads it back. */
+/* The parity the next served call will use (0 or 1), or HG_EINVAL (API page,
+ * HeadGather.__call__ source: a served call uses the current parity, then
+ * flips it; a declined call leaves it). With device-side parity on, this
+ * synchronises the device and reads it back. */
 int hg_parity(const hg_ctx *h);
 
 /*
@@ -232,57 +255,47 @@ int hg_set_vocab(hg_ctx *h, int vocab);
 int hg_vocab(const hg_ctx *h);
 
 /* Read-only view of one parity of the mailbox, for inspection by tests:
- * *dev = device address of [cap][tp*shard] BF16, *bytes = its size. */
+ * *dev = device address of [cap][tp*shard] BF16, *bytes = its size. The
+ * mailbox layout is the API page's (HeadGather.__init__ source: 2 parities
+ * x cap rows x shard/2*tp words); the pages expose no such view -- it exists
+ * so that tests can check that every served call leaves both parities
+ * all-sentinel. */
 int hg_mailbox(const hg_ctx *h, int parity, const void **dev, size_t *bytes);
 
 /* Enqueue a copy of one parity of the mailbox ([cap][tp*shard] BF16) into the
- * caller's device buffer `dst` (same size, must not overlap the mailbox). */
+ * caller's device buffer `dst` (same size, must not overlap the mailbox).
+ * An inspection aid like hg_mailbox; not on the pages. */
 int hg_copy_mailbox(const hg_ctx *h, int parity, void *dst, void *stream);
 
 /*
  * Bound every poll: a lane that re-reads a sentinel word more than `spins`
  * times gives up, counts a timeout in the context's status block and
  * continues (its output then holds sentinel words). 0 restores the default
- * (2^24 re-reads). Takes effect for calls enqueued afterwards.
+ * (2^24 re-reads). Takes effect for calls enqueued afterwards. Not on the
+ * pages, whose poll waits without bound (API page, module description); the
+ * bound keeps a missing push from hanging the device.
  */
 int hg_set_poll_limit(hg_ctx *h, unsigned long long spins);
 
 /* Wait for `stream`, then report and clear the poll-timeout count:
  * HG_OK if no poll gave up since the last check, HG_ETIMEOUT otherwise.
- * HG_EINVAL if the stream is capturing. */
+ * HG_EINVAL if the stream is capturing. The reporting side of the bounded
+ * poll (hg_set_poll_limit); not on the pages. */
 int hg_poll_status(hg_ctx *h, void *stream);
 
-/* Launch-shape knobs (for sweeps). Values are validated; 0 selects the
- * built-in choice where noted. */
-#define HG_TUNE_FUSED_BLOCK 1 /* threads per workgroup: 64, 128, 256, 512, 1024          */
-#define HG_TUNE_FUSED_VPT 2   /* 16-byte vectors per lane per chunk: 0 (auto), 1, 2, 4, 8 */
-#define HG_TUNE_FUSED_GRID 3  /* workgroup cap: 0 (4 per CU) or >= 1; never above the
-                                 co-resident limit                                      */
-#define HG_TUNE_SPLIT_BLOCK 4 /* as HG_TUNE_FUSED_BLOCK, for push / collect / stock      */
-#define HG_TUNE_SPLIT_VPT 5   /* as HG_TUNE_FUSED_VPT, for push / collect / stock        */
-#define HG_TUNE_POLL_SKEW 6   /* fused: workgroup b polls what (b-skew) mod grid pushed; 0: its own */
-#define HG_TUNE_PUSH_MODE 7   /* fused push: 0 two 64-bit agent-scope atomic stores;
-                                 1 plain 128-bit stores + an agent-scope release fence;
-                                 2 128-bit stores, agent-coherent (sc1) policy;
-                                 3 as 2 with the non-temporal hint                      */
-#define HG_TUNE_POLL_MODE 8   /* poll: 0 two 64-bit agent-scope atomic loads;
-                                 1 128-bit loads, agent-coherent (sc1) policy;
-                                 2 as 1 with the non-temporal hint                      */
-#define HG_TUNE_REARM_MODE 9  /* re-arm stores: 0 plain, 1 non-temporal                 */
-#define HG_TUNE_GEMM_VARIANT 10 /* hg_gemm_gather: lm_head implementation as for
-                                   hg_lmhead's `variant` (0: default)                 */
-int hg_set_tuning(hg_ctx *h, int knob, int value);
-int hg_get_tuning(const hg_ctx *h, int knob, int *value);
-
 /* Workgroups the fused kernel of an m-row call may keep resident at once on
- * the context's device with the current launch knobs (the grid cap), or a
- * negative code. */
+ * the context's device (its grid never exceeds this, so every workgroup whose
+ * pushes are awaited is running), or a negative code. Not on the pages: the
+ * grid sizing of the pages' kernel is not shown (API page, HeadGather.__init__
+ * source names only its per-row-count grid table). */
 int hg_fused_grid_limit(hg_ctx *h, int m);
 
-/* Static description of a status code. */
+/* Static description of a status code. Not on the pages (the pages report
+ * a failed build with a logged warning: API page, _install_gather source). */
 const char *hg_strerror(int code);
 
-/* The last HIP error seen by this thread inside the library ("" if none). */
+/* The last HIP error seen by this thread inside the library ("" if none).
+ * Not on the pages. */
 const char *hg_last_error_detail(void);
 
 #ifdef __cplusplus

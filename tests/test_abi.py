@@ -70,9 +70,6 @@ def test_null_context_paths():
     assert lib.hg_copy_mailbox(null, 0, ctypes.c_void_p(64), None) == _lib.HG_EINVAL
     assert lib.hg_set_poll_limit(null, 5) == _lib.HG_EINVAL
     assert lib.hg_poll_status(null, None) == _lib.HG_EINVAL
-    assert lib.hg_set_tuning(null, _lib.TUNE_FUSED_BLOCK, 256) == _lib.HG_EINVAL
-    v = ctypes.c_int()
-    assert lib.hg_get_tuning(null, _lib.TUNE_FUSED_BLOCK, ctypes.byref(v)) == _lib.HG_EINVAL
     assert lib.hg_fused_grid_limit(null, 1) == _lib.HG_EINVAL
     assert lib.hg_set_device_parity(null, 1, None) == _lib.HG_EINVAL
     assert lib.hg_set_vocab(null, 5) == _lib.HG_EINVAL
@@ -83,15 +80,19 @@ def test_stock_gather_argument_checks():
     lib = _lib.lib()
     ptrs = _lib.pointer_array([16, 32])
     out = ctypes.c_void_p(4096)
-    assert lib.hg_stock_gather(0, 8, ptrs, 1, out, None) == _lib.HG_EINVAL
-    assert lib.hg_stock_gather(2, 12, ptrs, 1, out, None) == _lib.HG_EINVAL
-    assert lib.hg_stock_gather(2, 8, ptrs, -1, out, None) == _lib.HG_EINVAL
-    assert lib.hg_stock_gather(2, 8, ptrs, 0, out, None) == _lib.HG_OK  # nothing to do
-    assert lib.hg_stock_gather(2, 8, ptrs, 1, ctypes.c_void_p(4100), None) == _lib.HG_EINVAL
-    bad = _lib.pointer_array([16, 40])  # misaligned rank-1 pointer
-    assert lib.hg_stock_gather(2, 8, bad, 1, out, None) == _lib.HG_EINVAL
+    assert lib.hg_stock_gather(0, 8, ptrs, 1, out, 8, None) == _lib.HG_EINVAL
+    assert lib.hg_stock_gather(2, 0, ptrs, 1, out, 1, None) == _lib.HG_EINVAL   # empty rows
+    assert lib.hg_stock_gather(2, 8, ptrs, -1, out, 16, None) == _lib.HG_EINVAL
+    assert lib.hg_stock_gather(2, 8, ptrs, 1, out, 0, None) == _lib.HG_EINVAL    # vocab < 1
+    assert lib.hg_stock_gather(2, 8, ptrs, 1, out, 17, None) == _lib.HG_EINVAL   # vocab > tp*shard
+    assert lib.hg_stock_gather(2, 8, ptrs, 0, out, 16, None) == _lib.HG_OK  # nothing to do
+    assert lib.hg_stock_gather(2, 8, ptrs, 1, ctypes.c_void_p(4100), 16, None) == _lib.HG_EINVAL
+    bad = _lib.pointer_array([16, 40])  # rank-1 pointer not 16-byte aligned (vector rows)
+    assert lib.hg_stock_gather(2, 8, bad, 1, out, 16, None) == _lib.HG_EINVAL
+    odd = _lib.pointer_array([16, 41])  # not even 2-byte aligned (element rows)
+    assert lib.hg_stock_gather(2, 12, odd, 1, out, 24, None) == _lib.HG_EINVAL
     overlap = _lib.pointer_array([16, 4096])  # rank 1 overlaps the output
-    assert lib.hg_stock_gather(2, 8, overlap, 1, out, None) == _lib.HG_EINVAL
+    assert lib.hg_stock_gather(2, 8, overlap, 1, out, 16, None) == _lib.HG_EINVAL
 
 
 def test_status_strings():
@@ -109,9 +110,9 @@ def test_fastcall_binding():
     assert f.gather(0, 0, 1, 0, 0) == _lib.HG_EINVAL
     assert f.push(0, 0, 1, 0) == _lib.HG_EINVAL
     assert f.collect(0, 1, 0, 0) == _lib.HG_EINVAL
-    assert f.stock(0, 8, 0, 1, 4096, 0) == _lib.HG_EINVAL  # tp 0
-    assert f.stock(2, 8, 0, 1, 4096, 0) == _lib.HG_EINVAL  # no shard array
-    assert f.stock(2, 8, 0, 0, 4096, 0) == _lib.HG_OK  # no rows: nothing to do
+    assert f.stock(0, 8, 0, 1, 4096, 8, 0) == _lib.HG_EINVAL  # tp 0
+    assert f.stock(2, 8, 0, 1, 4096, 16, 0) == _lib.HG_EINVAL  # no shard array
+    assert f.stock(2, 8, 0, 0, 4096, 16, 0) == _lib.HG_OK  # no rows: nothing to do
     with pytest.raises(TypeError):
         f.gather(0, 0, 1, 0)
     with pytest.raises(OverflowError):

@@ -173,15 +173,13 @@ def test_host_parity_still_declines_capture_and_mode_switch_rules():
     assert hg.parity == 1
 
 
-@pytest.mark.parametrize("fused_block,split_block", [(64, 1024), (1024, 64), (512, 128)])
-def test_graph_replays_across_block_sizes(fused_block, split_block):
-    """The parity slots are laid out per wave: the layout changes with the
-    waves per workgroup, from one (64 threads) to sixteen (1024)."""
-    tp, shard, cap = 4, 1024, 4
-    note(f"graph replays, fused block {fused_block}, split block {split_block}")
+@pytest.mark.parametrize("tp,shard,cap", [(4, 1024, 4), (8, 20480, 8), (2, 8, 3)])
+def test_graph_replays_across_grid_sizes(tp, shard, cap):
+    """The parity slots are laid out per wave of the launch that completes a
+    call: the layout changes with the grid, from one workgroup (TP=2, S=8) to
+    hundreds (TP=8, V=163840 at cap rows), between the calls of one replay."""
+    note(f"graph replays across grid sizes tp={tp} shard={shard} cap={cap}")
     hg, sim = make(tp, shard, cap), og.MailboxSim(tp, shard, cap)
-    hg.set_tuning(_lib.TUNE_FUSED_BLOCK, fused_block)
-    hg.set_tuning(_lib.TUNE_SPLIT_BLOCK, split_block)
     hg.set_device_parity(True)
     ms = [1, cap, 2]
     static_in = [dev(inputs(tp, shard, m, 600 + m)) for m in ms]

@@ -7,10 +7,9 @@ accesses through pointers. One case sits in each band, TP=8, V=163840:
 9830 rows (3.22 GB per call) and 13200 rows (4.33 GB), fused and split, two
 calls each (both parities), with 32-bit random words and injected sentinels.
 
-The whole output is checked on the GPU against the definition (rank-order
-concatenation, then every sentinel word rewritten to zero); sampled rows are
-checked against the CPU oracle; the used rows of the mailbox must be re-armed
-and the parity must alternate."""
+Every row of the output is checked against the CPU oracle
+(``oracle.gather.gather_definition``), 1024 rows at a time; the used rows of
+the mailbox must be re-armed and the parity must alternate."""
 
 from __future__ import annotations
 
@@ -50,15 +49,15 @@ def words_input(m: int, seed: int) -> torch.Tensor:
     return w.view(torch.bfloat16)
 
 
-def definition_on_gpu(shards: torch.Tensor) -> torch.Tensor:
-    cat = shards.permute(1, 0, 2).reshape(shards.shape[1], V).view(torch.int32)
-    return torch.where(cat == SENT, torch.zeros_like(cat), cat)
-
-
-def check_rows_against_oracle(out: torch.Tensor, shards: torch.Tensor, rows) -> None:
-    for r in rows:
-        want = og.gather_definition(list(syn.from_torch_bf16(shards[:, r:r + 1, :])))
-        assert np.array_equal(syn.from_torch_bf16(out[r:r + 1]), want), f"row {r}"
+def check_all_rows_against_oracle(out: torch.Tensor, shards: torch.Tensor, chunk: int = 1024):
+    m = out.shape[0]
+    for r0 in range(0, m, chunk):
+        r1 = min(m, r0 + chunk)
+        want = og.gather_definition(list(syn.from_torch_bf16(shards[:, r0:r1, :])))
+        got = syn.from_torch_bf16(out[r0:r1])
+        if not np.array_equal(got, want):
+            bad = np.argwhere(got != want)[0]
+            raise AssertionError(f"row {r0 + bad[0]} column {bad[1]} differs from the oracle")
 
 
 @pytest.mark.parametrize("variant", ["fused", "split"])
@@ -68,7 +67,6 @@ def test_largest_calls(m, variant):
     note(f"large rows m={m} ({m * ROW_BYTES / 1e9:.2f} GB per call) variant={variant}")
     hg = HeadGather(TP, SHARD, m, device=DEV)
     hg.set_poll_limit(1 << 20)
-    rows = [0, 1, m // 2, m - 2, m - 1]
     for call in range(2):
         shards = words_input(m, 1000 * m + call)
         assert hg.parity == call % 2
@@ -79,8 +77,7 @@ def test_largest_calls(m, variant):
             out = hg.collect(m)
         torch.cuda.synchronize()
         assert hg.poll_status() == _lib.HG_OK
-        assert torch.equal(out.view(torch.int32), definition_on_gpu(shards)), f"call {call}"
-        check_rows_against_oracle(out, shards, rows)
+        check_all_rows_against_oracle(out, shards)
         del out, shards
         used = hg.mailbox(call % 2).view(torch.int32)
         assert bool((used == SENT).all()), f"mailbox parity {call % 2} not re-armed"

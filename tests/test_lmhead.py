@@ -82,18 +82,16 @@ def test_hand_worked_golden_product():
     assert np.all(out[0, :, 4:] == 0)
 
 
-VARIANTS = [1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12]
-
-
-@pytest.mark.parametrize("variant", VARIANTS)
 @pytest.mark.parametrize("tp,shard,hidden,m", [
     (1, 32, 8, 1), (2, 64, 72, 3), (3, 288, 136, 17), (8, 96, 512, 256), (2, 512, 1032, 300),
-    (5, 160, 64, 255), (64, 32, 64, 2), (2, 256, 40, 7)])
-def test_ragged_sizes_against_oracle(tp, shard, hidden, m, variant):
-    note(f"lmhead ragged tp={tp} shard={shard} hidden={hidden} m={m} variant={variant}")
+    (5, 160, 64, 255), (64, 32, 64, 2), (2, 256, 40, 7), (2, 640, 256, 31), (2, 640, 256, 32),
+    (2, 640, 256, 33), (1, 960, 192, 63), (1, 960, 192, 64), (1, 960, 192, 65),
+    (3, 320, 200, 129), (4, 352, 264, 257), (2, 320, 7168, 4), (1, 1280, 128, 511)])
+def test_ragged_sizes_against_oracle(tp, shard, hidden, m):
+    note(f"lmhead ragged tp={tp} shard={shard} hidden={hidden} m={m}")
     x = rand_bits((m, hidden), 0.5, 10 + m)
     w = rand_bits((tp, shard, hidden), 0.5, 20 + hidden)
-    out = bits(lmhead(dev(x), dev(w), tp, shard, variant=variant))
+    out = bits(lmhead(dev(x), dev(w), tp, shard))
     for r in range(tp):
         assert_close_to_oracle(out[r], x, w[r])
 
@@ -136,11 +134,10 @@ def test_full_size_producer_gather_m256():
     # the product itself, rank by rank, against the float64 oracle
     for r in range(tp):
         assert_close_to_oracle(sb[r], x, w_host[r])
-    # deterministic: every implementation of the standalone product and a second
-    # producer call agree bit for bit
-    for variant in VARIANTS:
-        again = lmhead(xd, wd, tp, shard, variant=variant)
-        assert torch.equal(again.view(torch.int16), shards.view(torch.int16)), variant
+    # deterministic: the standalone product and a second producer call agree
+    # bit for bit
+    again = lmhead(xd, wd, tp, shard)
+    assert torch.equal(again.view(torch.int16), shards.view(torch.int16))
     out2 = hg.gemm_gather(xd, wd)
     assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
     assert hg.parity == 0 and hg.poll_status() == _lib.HG_OK
@@ -171,32 +168,59 @@ def test_producer_gather_declines_and_state():
 
 
 @pytest.mark.parametrize("m", [1, 5, 40])
-def test_producer_gather_every_variant_knob(m):
-    # hg_gemm_gather with each implementation chosen through the tuning knob:
-    # the same shards (bit for bit) and the gather of them, parity alternating
+def test_producer_gather_repeated_calls(m):
+    # hg_gemm_gather five times in a row: the shards it keeps equal the
+    # standalone product's bit for bit, the gather of them is bit-exact to the
+    # oracle's, and the parity alternates
     tp, shard, hidden, cap = 3, 96, 136, 64
-    note(f"producer variants m={m}")
+    note(f"producer repeated calls m={m}")
     x = dev(rand_bits((m, hidden), 0.5, 70 + m))
     w = dev(rand_bits((tp, shard, hidden), 0.5, 80 + m))
     hg = HeadGather(tp, shard, cap, device=DEV)
     hg.set_poll_limit(1 << 20)
     sim = og.MailboxSim(tp, shard, cap)
-    ref = None
-    for variant in [0] + VARIANTS:
-        hg.set_tuning(_lib.TUNE_GEMM_VARIANT, variant)
+    ref = lmhead(x, w, tp, shard)
+    for n in range(5):
         shards = torch.empty((tp, m, shard), dtype=torch.bfloat16, device=DEV)
         out = hg.gemm_gather(x, w, shards_out=shards)
-        if ref is None:
-            ref = shards.clone()
-        assert torch.equal(shards.view(torch.int16), ref.view(torch.int16)), variant
+        assert torch.equal(shards.view(torch.int16), ref.view(torch.int16)), n
         status, want = sim.gather(list(bits(shards)))
-        assert status == og.OK and np.array_equal(bits(out), want), variant
+        assert status == og.OK and np.array_equal(bits(out), want), n
         assert hg.parity == sim.parity
     assert hg.poll_status() == _lib.HG_OK
     for p in (0, 1):
         assert np.array_equal(bits(hg.mailbox(p)), sim.mailbox_bf16(p))
-    with pytest.raises(HgError):
-        hg.set_tuning(_lib.TUNE_GEMM_VARIANT, max(VARIANTS) + 1)
-    with pytest.raises(HgError):
-        hg.set_tuning(_lib.TUNE_GEMM_VARIANT, -1)
+    hg.close()
+
+
+def test_producer_epilogue_rewrites_a_sentinel_product():
+    """A product word equal to the sentinel pair (+0, -0) must reach the
+    mailbox as (+0, +0): otherwise the collect polls it until it gives up.
+    Column 0 of rank 0 has an all-zero weight row (its logit is +0); column 1
+    has one weight -2^-70 against x = 2^-70 in row 1, a product of -2^-140,
+    which rounds to BF16 -0 (below half the smallest BF16 subnormal, 2^-134)."""
+    tp, shard, hidden, cap, m = 2, 64, 72, 4, 3
+    note("producer epilogue: sentinel product word")
+    rng_x = rand_bits((m, hidden), 0.5, 5)
+    w = rand_bits((tp, shard, hidden), 0.5, 6)
+    w[0, 0, :] = 0x0000                      # column 0: +0 logits
+    w[0, 1, :] = 0x0000
+    w[0, 1, 0] = 0x9C80                      # -2^-70
+    rng_x[1, 0] = 0x1C80                     # +2^-70
+    assert ogemm.bf16_to_f64(np.array([0x9C80], np.uint16))[0] == -(2.0 ** -70)
+    x, wd = dev(rng_x), dev(w)
+    shards = lmhead(x, wd, tp, shard)
+    word = int(bits(shards)[0, 1, 0]) | (int(bits(shards)[0, 1, 1]) << 16)
+    assert word == og.SENT_WORD, hex(word)   # the product itself is the sentinel pair
+    hg = HeadGather(tp, shard, cap, device=DEV)
+    hg.set_poll_limit(1 << 16)
+    sim = og.MailboxSim(tp, shard, cap)
+    kept = torch.empty((tp, m, shard), dtype=torch.bfloat16, device=DEV)
+    out = hg.gemm_gather(x, wd, shards_out=kept)
+    assert torch.equal(kept.view(torch.int16), shards.view(torch.int16))  # kept as computed
+    got = bits(out)
+    assert got[1, 0] == 0 and got[1, 1] == 0                              # rewritten to (+0, +0)
+    status, want = sim.gather(list(bits(kept)))
+    assert status == og.OK and np.array_equal(got, want)
+    assert hg.poll_status() == _lib.HG_OK
     hg.close()

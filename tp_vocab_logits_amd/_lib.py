@@ -24,17 +24,6 @@ HG_ETIMEOUT = -4
 HG_ESTATE = -5
 HG_MAX_TP = 64
 
-TUNE_FUSED_BLOCK = 1
-TUNE_FUSED_VPT = 2
-TUNE_FUSED_GRID = 3
-TUNE_SPLIT_BLOCK = 4
-TUNE_SPLIT_VPT = 5
-TUNE_POLL_SKEW = 6
-TUNE_PUSH_MODE = 7
-TUNE_POLL_MODE = 8
-TUNE_REARM_MODE = 9
-TUNE_GEMM_VARIANT = 10
-
 _vp = ctypes.c_void_p
 _i = ctypes.c_int
 _ull = ctypes.c_ulonglong
@@ -50,8 +39,8 @@ SIGNATURES = {
     "hg_push": (_i, [_ctxp, ctypes.POINTER(_vp), _i, _vp]),
     "hg_push_ranks": (_i, [_ctxp, ctypes.POINTER(_vp), _i, _ull, _vp]),
     "hg_collect": (_i, [_ctxp, _i, _vp, _vp]),
-    "hg_stock_gather": (_i, [_i, _i, ctypes.POINTER(_vp), _i, _vp, _vp]),
-    "hg_lmhead": (_i, [_i, _i, _vp, ctypes.POINTER(_vp), _i, _i, ctypes.POINTER(_vp), _i, _vp]),
+    "hg_stock_gather": (_i, [_i, _i, ctypes.POINTER(_vp), _i, _vp, _i, _vp]),
+    "hg_lmhead": (_i, [_i, _i, _vp, ctypes.POINTER(_vp), _i, _i, ctypes.POINTER(_vp), _vp]),
     "hg_gemm_gather": (_i, [_ctxp, _vp, ctypes.POINTER(_vp), _i, _i, _vp, ctypes.POINTER(_vp), _vp]),
     "hg_parity": (_i, [_ctxp]),
     "hg_set_device_parity": (_i, [_ctxp, _i, _vp]),
@@ -61,8 +50,6 @@ SIGNATURES = {
     "hg_copy_mailbox": (_i, [_ctxp, _i, _vp, _vp]),
     "hg_set_poll_limit": (_i, [_ctxp, _ull]),
     "hg_poll_status": (_i, [_ctxp, _vp]),
-    "hg_set_tuning": (_i, [_ctxp, _i, _i]),
-    "hg_get_tuning": (_i, [_ctxp, _i, ctypes.POINTER(_i)]),
     "hg_fused_grid_limit": (_i, [_ctxp, _i]),
     "hg_strerror": (ctypes.c_char_p, [_i]),
     "hg_last_error_detail": (ctypes.c_char_p, []),

@@ -47,34 +47,15 @@ int hip_fail(hipError_t e, const char *where) {
     if (e_ != hipSuccess) return hip_fail(e_, #expr); \
   } while (0)
 
-// Launch defaults, chosen by sweeps on MI355X (TP=8, V=163840, M = 1..256):
+// Launch shape, chosen by sweeps on MI355X (TP=8, V=163840, M = 1..256):
 // 128-bit agent-coherent pushes and polls move the M=256 gather at about 85 %
 // of HBM peak against about 60 % for pairs of 64-bit atomics; four resident
-// 256-thread workgroups per CU beat the full co-resident grid; skew 1 keeps
-// every poll on data pushed by a workgroup on another XCD, within about
-// 0.1 us per M=1 call of self-polling.
-struct Tuning {
-  int fused_block = 256;
-  int fused_vpt = 0;   // 0: by row count
-  int fused_grid = 0;  // 0: kGridPerCu workgroups per CU, within the co-resident limit
-  int split_block = 256;
-  int split_vpt = 0;
-  int poll_skew = 1;
-  int push_mode = hg::kPushB128Sc1;
-  int poll_mode = hg::kPollB128Sc1Nt;
-  int rearm_mode = 1;
-  int gemm_variant = 0;  // lm_head implementation (hg::GemmVariant), 0: the default
-};
-
+// 256-thread workgroups per CU beat the full co-resident grid; a poll skew of
+// 1 keeps every poll on data pushed by a workgroup on another XCD, within
+// about 0.1 us per M=1 call of self-polling.
+constexpr int kBlock = 256;
 constexpr int kGridPerCu = 4;
-constexpr int kDefaultGemmVariant = hg::kGemmTile320Buf;
-
-bool valid_gemm_variant(int v) {
-  return v >= 0 && v <= hg::kGemmTile320Buf;
-}
-
-bool valid_block(int b) { return b == 64 || b == 128 || b == 256 || b == 512 || b == 1024; }
-bool valid_vpt(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8; }
+constexpr int kPollSkew = 1;
 
 // Vectors per lane for a launch moving `vectors` 16-byte vectors per phase:
 // one while the call is small (latency: spread it over many waves), two when
@@ -82,7 +63,7 @@ bool valid_vpt(int v) { return v == 0 || v == 1 || v == 2 || v == 4 || v == 8; }
 // with 256-thread workgroups (TP=8, V=163840): M=4 takes 4.22 us with one
 // against 4.48 with two; M=64 17.1 us with two against 18.4 with one and
 // 17.4 with four; M=256 61.8 us with two against 63.0 with four.
-int auto_vpt(long long vectors, int cus) {
+int mailbox_vpt(long long vectors, int cus) {
   const long long lanes = static_cast<long long>(cus) * 256;
   return vectors <= 4 * lanes ? 1 : 2;
 }
@@ -97,6 +78,7 @@ int stock_vpt(long long vectors, int cus) {
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned2(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 1u) == 0; }
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -119,9 +101,8 @@ struct hg_ctx {
   int pending_parity = 0;
   unsigned long long pending_ranks = 0;  // ranks that pushed into it
   unsigned long long poll_limit = kDefaultPollLimit;
-  Tuning tune;
-  // resident fused workgroups per CU at tune.fused_block, [log2 vpt][push][poll]; -1 unknown
-  int fused_per_cu[4][4][3];
+  // resident fused workgroups per CU, [vpt - 1][wide]; -1 unknown
+  int fused_per_cu[2][2];
 
   u32x4 *parity_box(int p) const { return box + static_cast<long long>(p) * cap * vv; }
   int *parity_slots() const { return reinterpret_cast<int *>(status + kSlotsOffset / 4); }
@@ -154,21 +135,13 @@ struct hg_ctx {
 
 namespace {
 
-int vpt_index(int vpt) { return vpt == 1 ? 0 : vpt == 2 ? 1 : vpt == 4 ? 2 : 3; }
-
-void forget_occupancy(hg_ctx *h) {
-  for (auto &a : h->fused_per_cu)
-    for (auto &b : a)
-      for (int &c : b) c = -1;
-}
-
-// Resident fused workgroups per CU for this variant at the current block size
-// (queried once per variant and block size).
+// Resident fused workgroups per CU for this variant (queried once per
+// variant).
 int fused_per_cu(hg_ctx *h, const hg::Modes &md, int *n) {
-  int &slot = h->fused_per_cu[vpt_index(md.vpt)][md.push][md.poll];
+  int &slot = h->fused_per_cu[md.vpt - 1][md.wide];
   if (slot < 0) {
     int v = 0;
-    HIP_TRY(hg::fused_blocks_per_cu(md, h->tp, h->tune.fused_block, &v));
+    HIP_TRY(hg::fused_blocks_per_cu(md, h->tp, kBlock, &v));
     slot = v;
   }
   *n = slot;
@@ -215,6 +188,24 @@ int load_shards(int tp, int shard, const void *const *shards, int m, unsigned lo
   return HG_OK;
 }
 
+// Workgroups of a fused launch: one per tile of 4 chunks, at most kGridPerCu
+// per CU and never more than can be resident at once (every workgroup whose
+// pushes are awaited must be running), nor more waves than parity slots.
+int fused_grid(hg_ctx *h, const hg::Modes &md, const Geometry &g, int *grid) {
+  const int waves = kBlock / 64;
+  const long long tiles = (static_cast<long long>(g.chunks) + waves - 1) / waves;
+  int per_cu = 0;
+  const int rc = fused_per_cu(h, md, &per_cu);
+  if (rc != HG_OK) return rc;
+  long long lim = static_cast<long long>(per_cu) * h->cus;
+  const long long want = static_cast<long long>(kGridPerCu) * h->cus;
+  if (want < lim) lim = want;
+  if (lim > hg::kParitySlots / waves) lim = hg::kParitySlots / waves;  // one slot per wave
+  if (lim < 1) return HG_EINVAL;
+  *grid = static_cast<int>(tiles < lim ? tiles : lim);
+  return HG_OK;
+}
+
 int split_grid(const hg_ctx *h, const Geometry &g, int block) {
   const int waves = block / 64;
   const long long tiles = (static_cast<long long>(g.chunks) + waves - 1) / waves;
@@ -223,23 +214,13 @@ int split_grid(const hg_ctx *h, const Geometry &g, int block) {
   return static_cast<int>(tiles < cap ? tiles : cap);
 }
 
-int pick_vpt(const hg_ctx *h, int knob, int m) {
-  return knob ? knob : auto_vpt(static_cast<long long>(m) * h->vv, h->cus);
-}
-
 // The kernel variant for an m-row call. The 128-bit coherent flavours address
 // the rows in use through a buffer resource with 32-bit offsets; a call whose
 // rows span 4 GiB or more uses the 64-bit atomic flavours instead.
-hg::Modes pick_modes(const hg_ctx *h, int vpt_knob, int m) {
+hg::Modes pick_modes(const hg_ctx *h, int m) {
   hg::Modes md;
-  md.vpt = pick_vpt(h, vpt_knob, m);
-  md.push = h->tune.push_mode;
-  md.poll = h->tune.poll_mode;
-  md.rearm_stream = h->tune.rearm_mode;
-  if (static_cast<unsigned long long>(m) * h->row_bytes() >= (1ull << 32)) {
-    if (md.push == hg::kPushB128Sc1 || md.push == hg::kPushB128Sc1Nt) md.push = hg::kPushAgent64;
-    md.poll = hg::kPollAgent64;
-  }
+  md.vpt = mailbox_vpt(static_cast<long long>(m) * h->vv, h->cus);
+  md.wide = static_cast<unsigned long long>(m) * h->row_bytes() >= (1ull << 32) ? 1 : 0;
   return md;
 }
 
@@ -311,7 +292,8 @@ HG_API int hg_create(int tp, int shard, int cap, hg_ctx **out) {
   }
   e = hipMemset(h->status, 0, kStatusBytes);
   if (e != hipSuccess) return fail(hip_fail(e, "hipMemset(status)"));
-  forget_occupancy(h);
+  for (auto &a : h->fused_per_cu)
+    for (int &c : a) c = -1;
   int rc = hg_arm(h, nullptr);
   if (rc != HG_OK) return fail(rc);
   e = hipDeviceSynchronize();
@@ -355,23 +337,14 @@ HG_API int hg_gather(hg_ctx *h, const void *const *shards, int m, void *out, voi
   int rc = check_call(h, shards, m, h ? all_ranks(h->tp) : 0, false, out, stream, &table);
   if (rc != HG_OK) return rc;
   if (!out) return HG_EINVAL;
-  const hg::Modes md = pick_modes(h, h->tune.fused_vpt, m);
+  const hg::Modes md = pick_modes(h, m);
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
-  const int waves = h->tune.fused_block / 64;
-  const long long tiles = (static_cast<long long>(g.chunks) + waves - 1) / waves;
-  int per_cu = 0;
-  rc = fused_per_cu(h, md, &per_cu);
+  int grid = 0;
+  rc = fused_grid(h, md, g, &grid);
   if (rc != HG_OK) return rc;
-  long long lim = static_cast<long long>(per_cu) * h->cus;
-  const long long want = h->tune.fused_grid > 0 ? h->tune.fused_grid
-                                                : static_cast<long long>(kGridPerCu) * h->cus;
-  if (want < lim) lim = want;
-  if (lim > hg::kParitySlots / waves) lim = hg::kParitySlots / waves;  // one slot per wave
-  if (lim < 1) return HG_EINVAL;
-  const int grid = static_cast<int>(tiles < lim ? tiles : lim);
-  const hg::ParityArg pa = h->parity_arg(h->parity, true, grid, h->tune.fused_block);
+  const hg::ParityArg pa = h->parity_arg(h->parity, true, grid, kBlock);
   HIP_TRY(hg::launch_fused(table, g, md, pa, used_box_bytes(h, m), h->out_rows(out), h->status,
-                           h->poll_limit, h->tune.poll_skew % grid, grid, h->tune.fused_block,
+                           h->poll_limit, kPollSkew % grid, grid, kBlock,
                            static_cast<hipStream_t>(stream)));
   if (!h->dev_parity) h->parity ^= 1;
   return HG_OK;
@@ -382,12 +355,11 @@ HG_API int hg_push_ranks(hg_ctx *h, const void *const *shards, int m, unsigned l
   ShardTable table;
   int rc = check_call(h, shards, m, ranks, true, nullptr, stream, &table);
   if (rc != HG_OK) return rc;
-  const int vpt = pick_vpt(h, h->tune.split_vpt, m);
+  const int vpt = pick_modes(h, m).vpt;
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, vpt);
-  const int block = h->tune.split_block;
   const int p = h->pending_m >= 0 ? h->pending_parity : h->parity;
-  HIP_TRY(hg::launch_push(table, g, vpt, h->parity_arg(p, false), ranks, split_grid(h, g, block),
-                          block, static_cast<hipStream_t>(stream)));
+  HIP_TRY(hg::launch_push(table, g, vpt, h->parity_arg(p, false), ranks, split_grid(h, g, kBlock),
+                          kBlock, static_cast<hipStream_t>(stream)));
   h->pending_m = m;
   h->pending_parity = p;
   h->pending_ranks |= ranks;
@@ -411,13 +383,12 @@ HG_API int hg_collect(hg_ctx *h, int m, void *out, void *stream) {
   const size_t out_bytes = static_cast<size_t>(m) * h->out_row_bytes();
   const size_t box_bytes = static_cast<size_t>(2) * h->cap * h->row_bytes();
   if (!out || !aligned16(out) || overlaps(out, out_bytes, h->box, box_bytes)) return HG_EINVAL;
-  const hg::Modes md = pick_modes(h, h->tune.split_vpt, m);
+  const hg::Modes md = pick_modes(h, m);
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
-  const int block = h->tune.split_block;
-  const int grid = split_grid(h, g, block);
-  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->pending_parity, true, grid, block),
+  const int grid = split_grid(h, g, kBlock);
+  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->pending_parity, true, grid, kBlock),
                              used_box_bytes(h, m), h->out_rows(out), h->status, h->poll_limit,
-                             grid, block, static_cast<hipStream_t>(stream)));
+                             grid, kBlock, static_cast<hipStream_t>(stream)));
   h->pending_m = -1;
   h->pending_ranks = 0;
   if (!h->dev_parity) h->parity = h->pending_parity ^ 1;
@@ -425,27 +396,48 @@ HG_API int hg_collect(hg_ctx *h, int m, void *out, void *stream) {
 }
 
 HG_API int hg_stock_gather(int tp, int shard, const void *const *shards, int m, void *out,
-                           void *stream) {
-  if (tp < 1 || tp > HG_MAX_TP || shard < 8 || shard % 8 != 0 || m < 0) return HG_EINVAL;
+                           int vocab, void *stream) {
+  if (tp < 1 || tp > HG_MAX_TP || shard < 1 || m < 0) return HG_EINVAL;
+  const long long width = static_cast<long long>(tp) * shard;
+  if (vocab < 1 || vocab > width) return HG_EINVAL;
   if (m == 0) return HG_OK;
-  if (!out || !aligned16(out)) return HG_EINVAL;
-  const long long vv = static_cast<long long>(tp) * (shard / 8);
-  if (vv * m >= (1ll << 31)) return HG_EINVAL;
+  if (static_cast<long long>(m) * width >= (1ll << 34)) return HG_EINVAL;
+  const bool vec = shard % 8 == 0;  // whole 16-byte vectors per shard row
+  if (!out || !(vec ? aligned16(out) : aligned2(out))) return HG_EINVAL;
+  if (!shards) return HG_EINVAL;
   ShardTable table;
-  const size_t out_bytes = static_cast<size_t>(m) * vv * 16;
-  int rc = load_shards(tp, shard, shards, m, all_ranks(tp), &table, out, out_bytes, nullptr, 0);
-  if (rc != HG_OK) return rc;
+  memset(&table, 0, sizeof table);
+  const size_t out_bytes = static_cast<size_t>(m) * vocab * 2;
+  const size_t shard_bytes = static_cast<size_t>(m) * shard * 2;
+  for (int r = 0; r < tp; ++r) {
+    const void *p = shards[r];
+    if (!p || !(vec ? aligned16(p) : aligned2(p)) || overlaps(p, shard_bytes, out, out_bytes))
+      return HG_EINVAL;
+    table.p[r] = static_cast<const u32x4 *>(p);
+  }
   int dev = 0, cus = 0;
   HIP_TRY(hipGetDevice(&dev));
   HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (!vec) {
+    const long long n = static_cast<long long>(m) * vocab;
+    long long grid = (n + 255) / 256;
+    if (grid > static_cast<long long>(cus) * 8) grid = static_cast<long long>(cus) * 8;
+    HIP_TRY(hg::launch_stock_elem(table, tp, shard, m, static_cast<unsigned short *>(out), vocab,
+                                  static_cast<int>(grid), 256, s));
+    return HG_OK;
+  }
+  const long long vv = width / 8;
+  if (vv * m >= (1ll << 31)) return HG_EINVAL;
   const int vpt = stock_vpt(m * vv, cus);
   const Geometry g = hg::make_geometry(tp, shard, m, vpt);
-  const int block = 256;
   const long long tiles = (static_cast<long long>(g.chunks) + 3) / 4;
   const long long cap = static_cast<long long>(cus) * 16;
-  HIP_TRY(hg::launch_stock(table, g, vpt, static_cast<u32x4 *>(out),
-                           static_cast<int>(tiles < cap ? tiles : cap), block,
-                           static_cast<hipStream_t>(stream)));
+  hg::OutRows o;
+  o.ptr = static_cast<u32x4 *>(out);
+  o.cols = vocab;
+  o.cvec = vocab % 8 == 0 ? vocab / 8 : 0;
+  HIP_TRY(hg::launch_stock(table, g, vpt, o, static_cast<int>(tiles < cap ? tiles : cap), 256, s));
   return HG_OK;
 }
 
@@ -481,8 +473,8 @@ int check_lmhead(int tp, int shard, const void *x, const void *const *w, int hid
 }  // namespace
 
 HG_API int hg_lmhead(int tp, int shard, const void *x, const void *const *w, int hidden, int m,
-                     void *const *shards_out, int variant, void *stream) {
-  if (!shards_out || !valid_gemm_variant(variant)) return HG_EINVAL;
+                     void *const *shards_out, void *stream) {
+  if (!shards_out) return HG_EINVAL;
   ShardTable wt;
   hg::OutTable ot;
   const int rc = check_lmhead(tp, shard, x, w, hidden, m, shards_out, &wt, &ot);
@@ -490,8 +482,7 @@ HG_API int hg_lmhead(int tp, int shard, const void *x, const void *const *w, int
   if (m == 0) return HG_OK;
   hg::ParityArg none = {};
   HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, true, false, none, m, hidden,
-                            shard, tp, variant ? variant : kDefaultGemmVariant,
-                            static_cast<hipStream_t>(stream)));
+                            shard, tp, static_cast<hipStream_t>(stream)));
   return HG_OK;
 }
 
@@ -509,22 +500,32 @@ HG_API int hg_gemm_gather(hg_ctx *h, const void *x, const void *const *w, int hi
   hg::OutTable ot;
   rc = check_lmhead(h->tp, h->shard, x, w, hidden, m, shards_out, &wt, &ot);
   if (rc != HG_OK) return rc;
+  // out, the mailbox, x, the weights and the shard copies must not overlap
+  // one another (the shard copies are already checked against x and w)
   const size_t out_bytes = static_cast<size_t>(m) * h->out_row_bytes();
   const size_t box_bytes = static_cast<size_t>(2) * h->cap * h->row_bytes();
+  const size_t w_bytes = static_cast<size_t>(h->shard) * hidden * 2;
+  const size_t so_bytes = static_cast<size_t>(m) * h->shard * 2;
   if (!out || !aligned16(out) || overlaps(out, out_bytes, h->box, box_bytes) ||
-      overlaps(out, out_bytes, x, static_cast<size_t>(m) * hidden * 2))
+      overlaps(out, out_bytes, x, static_cast<size_t>(m) * hidden * 2) ||
+      overlaps(x, static_cast<size_t>(m) * hidden * 2, h->box, box_bytes))
     return HG_EINVAL;
+  for (int r = 0; r < h->tp; ++r) {
+    if (overlaps(out, out_bytes, w[r], w_bytes) || overlaps(w[r], w_bytes, h->box, box_bytes))
+      return HG_EINVAL;
+    if (shards_out && (overlaps(shards_out[r], so_bytes, h->box, box_bytes) ||
+                       overlaps(shards_out[r], so_bytes, out, out_bytes)))
+      return HG_EINVAL;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   HIP_TRY(hg::launch_lmhead(static_cast<const u32x4 *>(x), wt, ot, shards_out != nullptr, true,
-                            h->parity_arg(h->parity, false), m, hidden, h->shard, h->tp,
-                            h->tune.gemm_variant ? h->tune.gemm_variant : kDefaultGemmVariant, s));
-  const hg::Modes md = pick_modes(h, h->tune.split_vpt, m);
+                            h->parity_arg(h->parity, false), m, hidden, h->shard, h->tp, s));
+  const hg::Modes md = pick_modes(h, m);
   const Geometry g = hg::make_geometry(h->tp, h->shard, m, md.vpt);
-  const int block = h->tune.split_block;
-  const int grid = split_grid(h, g, block);
-  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->parity, true, grid, block),
+  const int grid = split_grid(h, g, kBlock);
+  HIP_TRY(hg::launch_collect(g, md, h->parity_arg(h->parity, true, grid, kBlock),
                              used_box_bytes(h, m), h->out_rows(out), h->status, h->poll_limit,
-                             grid, block, s));
+                             grid, kBlock, s));
   if (!h->dev_parity) h->parity ^= 1;
   return HG_OK;
 }
@@ -609,76 +610,10 @@ HG_API int hg_poll_status(hg_ctx *h, void *stream) {
   return HG_ETIMEOUT;
 }
 
-HG_API int hg_set_tuning(hg_ctx *h, int knob, int value) {
-  if (!h) return HG_EINVAL;
-  switch (knob) {
-    case HG_TUNE_FUSED_BLOCK:
-      if (!valid_block(value)) return HG_EINVAL;
-      h->tune.fused_block = value;
-      forget_occupancy(h);
-      return HG_OK;
-    case HG_TUNE_FUSED_VPT:
-      if (!valid_vpt(value)) return HG_EINVAL;
-      h->tune.fused_vpt = value;
-      return HG_OK;
-    case HG_TUNE_FUSED_GRID:
-      if (value < 0) return HG_EINVAL;
-      h->tune.fused_grid = value;
-      return HG_OK;
-    case HG_TUNE_SPLIT_BLOCK:
-      if (!valid_block(value)) return HG_EINVAL;
-      h->tune.split_block = value;
-      return HG_OK;
-    case HG_TUNE_SPLIT_VPT:
-      if (!valid_vpt(value)) return HG_EINVAL;
-      h->tune.split_vpt = value;
-      return HG_OK;
-    case HG_TUNE_POLL_SKEW:
-      if (value < 0) return HG_EINVAL;
-      h->tune.poll_skew = value;
-      return HG_OK;
-    case HG_TUNE_PUSH_MODE:
-      if (value < hg::kPushAgent64 || value > hg::kPushB128Sc1Nt) return HG_EINVAL;
-      h->tune.push_mode = value;
-      return HG_OK;
-    case HG_TUNE_POLL_MODE:
-      if (value < hg::kPollAgent64 || value > hg::kPollB128Sc1Nt) return HG_EINVAL;
-      h->tune.poll_mode = value;
-      return HG_OK;
-    case HG_TUNE_REARM_MODE:
-      if (value != 0 && value != 1) return HG_EINVAL;
-      h->tune.rearm_mode = value;
-      return HG_OK;
-    case HG_TUNE_GEMM_VARIANT:
-      if (!valid_gemm_variant(value)) return HG_EINVAL;
-      h->tune.gemm_variant = value;
-      return HG_OK;
-    default:
-      return HG_EINVAL;
-  }
-}
-
-HG_API int hg_get_tuning(const hg_ctx *h, int knob, int *value) {
-  if (!h || !value) return HG_EINVAL;
-  switch (knob) {
-    case HG_TUNE_FUSED_BLOCK: *value = h->tune.fused_block; return HG_OK;
-    case HG_TUNE_FUSED_VPT: *value = h->tune.fused_vpt; return HG_OK;
-    case HG_TUNE_FUSED_GRID: *value = h->tune.fused_grid; return HG_OK;
-    case HG_TUNE_SPLIT_BLOCK: *value = h->tune.split_block; return HG_OK;
-    case HG_TUNE_SPLIT_VPT: *value = h->tune.split_vpt; return HG_OK;
-    case HG_TUNE_POLL_SKEW: *value = h->tune.poll_skew; return HG_OK;
-    case HG_TUNE_PUSH_MODE: *value = h->tune.push_mode; return HG_OK;
-    case HG_TUNE_POLL_MODE: *value = h->tune.poll_mode; return HG_OK;
-    case HG_TUNE_REARM_MODE: *value = h->tune.rearm_mode; return HG_OK;
-    case HG_TUNE_GEMM_VARIANT: *value = h->tune.gemm_variant; return HG_OK;
-    default: return HG_EINVAL;
-  }
-}
-
 HG_API int hg_fused_grid_limit(hg_ctx *h, int m) {
   if (!h || m < 1 || m > h->cap) return HG_EINVAL;
   int per_cu = 0;
-  const int rc = fused_per_cu(h, pick_modes(h, h->tune.fused_vpt, m), &per_cu);
+  const int rc = fused_per_cu(h, pick_modes(h, m), &per_cu);
   if (rc != HG_OK) return rc;
   return per_cu * h->cus;
 }

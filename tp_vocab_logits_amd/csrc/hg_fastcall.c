@@ -17,7 +17,7 @@ typedef int (*gather_fn)(void *h, const void *const *shards, int m, void *out, v
 typedef int (*push_fn)(void *h, const void *const *shards, int m, void *stream);
 typedef int (*collect_fn)(void *h, int m, void *out, void *stream);
 typedef int (*stock_fn)(int tp, int shard, const void *const *shards, int m, void *out,
-                        void *stream);
+                        int vocab, void *stream);
 
 static gather_fn g_gather;
 static push_fn g_push;
@@ -110,16 +110,17 @@ static PyObject *py_collect(PyObject *self, PyObject *const *args, Py_ssize_t na
   return PyLong_FromLong(g_collect(h, m, out, stream));
 }
 
-/* stock(tp, shard, shards_array_addr, m, out_addr, stream) -> status */
+/* stock(tp, shard, shards_array_addr, m, out_addr, vocab, stream) -> status */
 static PyObject *py_stock(PyObject *self, PyObject *const *args, Py_ssize_t nargs) {
   void *shards, *out, *stream;
-  int tp, shard, m;
+  int tp, shard, m, vocab;
   (void)self;
-  if (!check_bound((void *)g_stock, nargs, 6)) return NULL;
+  if (!check_bound((void *)g_stock, nargs, 7)) return NULL;
   if (!as_int(args[0], &tp) || !as_int(args[1], &shard) || !as_ptr(args[2], &shards) ||
-      !as_int(args[3], &m) || !as_ptr(args[4], &out) || !as_ptr(args[5], &stream))
+      !as_int(args[3], &m) || !as_ptr(args[4], &out) || !as_int(args[5], &vocab) ||
+      !as_ptr(args[6], &stream))
     return NULL;
-  return PyLong_FromLong(g_stock(tp, shard, (const void *const *)shards, m, out, stream));
+  return PyLong_FromLong(g_stock(tp, shard, (const void *const *)shards, m, out, vocab, stream));
 }
 
 static PyMethodDef methods[] = {
@@ -132,7 +133,7 @@ static PyMethodDef methods[] = {
     {"collect", (PyCFunction)(void (*)(void))py_collect, METH_FASTCALL,
      "collect(handle, m, out_addr, stream) -> status"},
     {"stock", (PyCFunction)(void (*)(void))py_stock, METH_FASTCALL,
-     "stock(tp, shard, shards_addr, m, out_addr, stream) -> status"},
+     "stock(tp, shard, shards_addr, m, out_addr, vocab, stream) -> status"},
     {NULL, NULL, 0, NULL},
 };
 

@@ -55,29 +55,25 @@ struct Geometry {
 
 Divisor make_divisor(unsigned d);
 
-// How the fused push makes its mailbox stores visible to pollers in other
-// workgroups of the same kernel.
+// How a launch makes mailbox stores visible to pollers in other workgroups of
+// the same kernel, and how a poll reads the mailbox. The 128-bit flavour
+// addresses the rows of a call through a buffer resource with 32-bit offsets;
+// a call whose rows span 4 GiB or more takes the 64-bit atomic flavour.
 enum PushMode : int {
   kPushAgent64 = 0,    // 2 x 64-bit relaxed agent-scope atomic stores
-  kPushPlain = 1,      // plain 128-bit stores, one agent-scope release fence per wave
-  kPushB128Sc1 = 2,    // 128-bit stores with the agent-coherence (sc1) cache policy
-  kPushB128Sc1Nt = 3,  // the same with the non-temporal hint
-  kPushStream = 4,     // 128-bit non-temporal stores, visible at kernel end (split push)
+  kPushB128Sc1 = 1,    // 128-bit stores with the agent-coherence (sc1) cache policy
+  kPushStream = 2,     // 128-bit non-temporal stores, visible at kernel end (split push)
 };
 
-// How a poll reads the mailbox.
 enum PollMode : int {
   kPollAgent64 = 0,    // 2 x 64-bit relaxed agent-scope atomic loads
-  kPollB128Sc1 = 1,    // 128-bit loads with the agent-coherence (sc1) cache policy
-  kPollB128Sc1Nt = 2,  // the same with the non-temporal hint
+  kPollB128Sc1Nt = 1,  // 128-bit loads with the sc1 policy and the non-temporal hint
 };
 
 // Kernel variant of one launch.
 struct Modes {
-  int vpt;           // 16-byte vectors per lane per chunk: 1, 2, 4, 8
-  int push;          // PushMode (fused kernel)
-  int poll;          // PollMode
-  int rearm_stream;  // re-arm with non-temporal stores (1) or plain stores (0)
+  int vpt;   // 16-byte vectors per lane per chunk: 1 or 2 (1, 2 or 4 for the stock copy)
+  int wide;  // rows span 4 GiB or more: 64-bit atomic push and poll
 };
 
 // Where the copy step writes. Row i of the gathered logits goes to
@@ -153,33 +149,23 @@ hipError_t launch_push(const ShardTable &sh, const Geometry &g, int vpt, const P
 hipError_t launch_collect(const Geometry &g, const Modes &md, const ParityArg &pa,
                           unsigned box_bytes, const OutRows &out, unsigned *status,
                           unsigned long long limit, int grid, int block, hipStream_t s);
-hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *out, int grid,
-                        int block, hipStream_t s);
+// The stock concatenation into `out` (its columns below out.cols), in 16-byte
+// vectors.
+hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, const OutRows &out,
+                        int grid, int block, hipStream_t s);
+// The same for shards whose rows are not a whole number of 16-byte vectors,
+// element by element (2-byte units): out[i][j] for j < cols, row stride cols.
+hipError_t launch_stock_elem(const ShardTable &sh, int tp, int shard, int m, unsigned short *out,
+                             int cols, int grid, int block, hipStream_t s);
 
 // The lm_head shard product X [m][hidden] @ W_r^T (W_r = w.p[r], [shard][hidden]),
 // BF16 in, fp32 accumulate, BF16 out. `box` (mailbox rows of the current
 // parity, [m][tp*shard] words) receives the words with the sentinel
-// rewritten, when non-null; `shards_out` receives the plain BF16 shards when
-// `keep`. Needs shard % 32 == 0 and hidden % 8 == 0. `variant` picks the
-// implementation (all give the same bits).
-enum GemmVariant : int {
-  kGemmDirectLds = 1,  // 256 columns per workgroup, global -> LDS loads, 4 stages
-  kGemmStaged256 = 2,  // 256 columns per workgroup, loads staged through registers
-  kGemmStaged128 = 3,  // 128 columns per workgroup, loads staged through registers
-  kGemmDirectLdsNt = 4,    // as 1, weight loads non-temporal
-  kGemmDirectLds64 = 5,    // as 1 with 64-wide K steps, 2 stages
-  kGemmDirectLds64Nt = 6,  // as 5, weight loads non-temporal
-  kGemmDirectLdsDeepW = 7,  // 64-wide K steps, 2 X stages + 3 weight stages, weights nt
-  kGemmWave128 = 8,  // as 7 with four waves of 128 x 128 instead of eight of 128 x 64
-  kGemmTile320 = 9,  // 320 columns per workgroup, eight waves of 64 x 160, 64-wide K, 2 stages
-  kGemmTile320K32 = 10,    // as 9 with 32-wide K steps and 4 stages
-  kGemmTile320K32S3 = 11,  // as 9 with 32-wide K steps and 3 stages
-  kGemmTile320Buf = 12,    // as 9 with buffer loads into LDS
-};
-// `box` (when `push`) selects the mailbox rows through a ParityArg.
+// rewritten, when `push`; `shards_out` receives the plain BF16 shards when
+// `keep`. Needs shard % 32 == 0 and hidden % 8 == 0.
 hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &shards_out, bool keep,
                          bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
-                         int variant, hipStream_t s);
+                         hipStream_t s);
 
 // Resident workgroups per CU of the fused kernel variant at a block size.
 hipError_t fused_blocks_per_cu(const Modes &md, int tp, int block, int *blocks);

@@ -23,13 +23,13 @@
 //
 // Visibility inside one kernel. The eight XCDs of an MI355X each have their
 // own L2, so a mailbox word pushed by one workgroup reaches a poller on another
-// XCD only through memory-side caches or HBM. Pushes therefore use stores with
-// agent scope -- relaxed 64-bit atomics, or 128-bit stores carrying the same
-// `sc1` cache-policy bit the compiler gives agent-scope atomics -- or plain
-// stores followed by one agent-scope release fence; polls use loads with agent
-// scope (64-bit relaxed atomics or 128-bit `sc1` loads), so a re-read never
-// returns a stale line of the poller's own L1 or L2. Every 32-bit word is
-// written and read whole, and the poll tests every word of a vector.
+// XCD only through memory-side caches or HBM. Pushes therefore use 128-bit
+// stores carrying the same `sc1` cache-policy bit the compiler gives
+// agent-scope atomics, and polls 128-bit `sc1` loads, so a re-read never
+// returns a stale line of the poller's own L1 or L2. Calls whose rows span
+// 4 GiB or more (past the 32-bit offsets of a buffer resource) use pairs of
+// relaxed 64-bit agent-scope atomics instead. Every 32-bit word is written and
+// read whole, and the poll tests every word of a vector.
 
 #include "hg_internal.h"
 
@@ -41,7 +41,7 @@ constexpr int kWave = 64;
 
 // Buffer-resource word 3 for raw 32-bit data on the gfx9 family (gfx950).
 constexpr int kRawBufferWord3 = 0x00020000;
-// Cache-policy operand of the buffer intrinsics on gfx94x/gfx950.
+// Cache-policy operand of the buffer intrinsics on gfx950.
 constexpr int kPolicySc1 = 16;
 constexpr int kPolicyNt = 2;
 
@@ -107,13 +107,8 @@ template <int STORE>
 __device__ __forceinline__ void box_store(const Box &b, long long idx, u32x4 v) {
   if constexpr (STORE == kPushAgent64) {
     store_agent64(b.ptr + idx, v);
-  } else if constexpr (STORE == kPushPlain) {
-    b.ptr[idx] = v;
   } else if constexpr (STORE == kPushB128Sc1) {
     __builtin_amdgcn_raw_buffer_store_b128(v, b.rsrc, static_cast<int>(idx * 16), 0, kPolicySc1);
-  } else if constexpr (STORE == kPushB128Sc1Nt) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, b.rsrc, static_cast<int>(idx * 16), 0,
-                                           kPolicySc1 | kPolicyNt);
   } else {
     store_stream(b.ptr + idx, v);
   }
@@ -123,8 +118,6 @@ template <int POLL>
 __device__ __forceinline__ u32x4 box_load(const Box &b, long long idx) {
   if constexpr (POLL == kPollAgent64) {
     return load_agent64(b.ptr + idx);
-  } else if constexpr (POLL == kPollB128Sc1) {
-    return __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, static_cast<int>(idx * 16), 0, kPolicySc1);
   } else {
     return __builtin_amdgcn_raw_buffer_load_b128(b.rsrc, static_cast<int>(idx * 16), 0,
                                                  kPolicySc1 | kPolicyNt);
@@ -241,12 +234,11 @@ __device__ __forceinline__ u32x4 await_vec(const Box &b, long long idx, u32x4 v,
   return v;
 }
 
-__device__ __forceinline__ void rearm_store(const Box &b, long long idx, bool stream) {
+// Re-arm one mailbox vector (non-temporal: the rows are next read by a later
+// call, after the kernel boundary).
+__device__ __forceinline__ void rearm_store(const Box &b, long long idx) {
   const u32x4 armed = {kSentinel, kSentinel, kSentinel, kSentinel};
-  if (stream)
-    store_stream(b.ptr + idx, armed);
-  else
-    b.ptr[idx] = armed;
+  store_stream(b.ptr + idx, armed);
 }
 
 // Copy one polled vector (BF16 columns 8*cv .. 8*cv+7 of gathered row `row`)
@@ -270,7 +262,7 @@ __device__ __forceinline__ void out_store(const OutRows &o, int row, int cv, u32
 template <int VPT, int POLL>
 __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane, const Box &box,
                                               const OutRows &out, unsigned *status,
-                                              PollBudget &bud, bool rearm_stream) {
+                                              PollBudget &bud) {
   const ChunkPos p = chunk_pos(c, g, VPT);
   const long long d = p.base + p.k0 + lane;
   const int cv = p.rank * g.sv + p.k0 + lane;  // column vector of the output row
@@ -283,7 +275,7 @@ __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       out_store(out, p.row, cv + i * kWave, v[i]);
-      rearm_store(box, d + i * kWave, rearm_stream);
+      rearm_store(box, d + i * kWave);
     }
   } else {
     const int left = g.sv - p.k0 - lane;
@@ -293,7 +285,7 @@ __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane
         const long long idx = d + i * kWave;
         const u32x4 v = await_vec<POLL>(box, idx, box_load<POLL>(box, idx), status, bud);
         out_store(out, p.row, cv + i * kWave, v);
-        rearm_store(box, idx, rearm_stream);
+        rearm_store(box, idx);
       }
     }
   }
@@ -387,8 +379,7 @@ __global__ __launch_bounds__(1024) void k_arm(u32x4 *box, long long vectors, int
 template <int VPT, int PUSH, int POLL, int NT>
 __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, ParityArg pa,
                                                 unsigned box_bytes, OutRows out, unsigned *status,
-                                                unsigned long long limit, int skew,
-                                                int rearm_stream) {
+                                                unsigned long long limit, int skew) {
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
@@ -410,14 +401,13 @@ __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, 
     const int c = t * waves + wave;
     if (c < g.chunks) push_chunk<VPT, true, PUSH>(sh, g, c, lane, box);
   }
-  if constexpr (PUSH == kPushPlain) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
 
   PollBudget bud{0ull, limit, false};
   // skew is in [0, grid) (the host reduces it)
   const int from = me >= skew ? me - skew : me - skew + grid;
   for (int t = from; t < tiles; t += grid) {
     const int c = t * waves + wave;
-    if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud, rearm_stream);
+    if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud);
   }
   pass_parity(pa, np);
 }
@@ -446,7 +436,7 @@ __global__ __launch_bounds__(1024) void k_push(ShardTableN<NT> sh, Geometry g, P
 template <int VPT, int POLL>
 __global__ __launch_bounds__(1024) void k_collect(Geometry g, ParityArg pa, unsigned box_bytes,
                                                   OutRows out, unsigned *status,
-                                                  unsigned long long limit, int rearm_stream) {
+                                                  unsigned long long limit) {
   const NextParity np = take_parity(pa);
   u32x4 *box_ptr = pa.box + np.p * pa.stride;
   const int waves = waves_per_block();
@@ -457,7 +447,7 @@ __global__ __launch_bounds__(1024) void k_collect(Geometry g, ParityArg pa, unsi
   PollBudget bud{0ull, limit, false};
   for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
     const int c = t * waves + wave;
-    if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud, rearm_stream);
+    if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud);
   }
   pass_parity(pa, np);
 }
@@ -469,30 +459,65 @@ __global__ __launch_bounds__(256) void k_set_slots(int *slots, int value) {
 }
 
 // The stock path's single-device share: rank-order concatenation, bytes
-// unchanged.
+// unchanged, into the first out.cols columns of each output row.
 template <int VPT, int NT>
-__global__ __launch_bounds__(1024) void k_stock(ShardTableN<NT> sh, Geometry g, u32x4 *out) {
+__global__ __launch_bounds__(1024) void k_stock(ShardTableN<NT> sh, Geometry g, OutRows out) {
   const int waves = waves_per_block();
   const int wave = wave_id();
   const int lane = lane_id();
   const int tiles = tile_count(g, waves);
-  const Box dst = pointer_box(out);
   for (int t = blockIdx.x; t < tiles; t += gridDim.x) {
     const int c = t * waves + wave;
-    if (c < g.chunks) push_chunk<VPT, false, kPushStream>(sh, g, c, lane, dst);
+    if (c >= g.chunks) continue;
+    const ChunkPos p = chunk_pos(c, g, VPT);
+    const u32x4 *src = sh.p[p.rank] + static_cast<long long>(p.row) * g.sv + p.k0 + lane;
+    const int cv = p.rank * g.sv + p.k0 + lane;
+    const int left = g.sv - p.k0 - lane;
+    u32x4 v[VPT];
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) v[i] = i * kWave < left ? load_stream(src + i * kWave) : u32x4{};
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (i * kWave < left) out_store(out, p.row, cv + i * kWave, v[i]);
+  }
+}
+
+// The stock concatenation for rows that are not a whole number of 16-byte
+// vectors: one 2-byte element per lane and step, out[i][j] for j < cols.
+template <int NT>
+__global__ __launch_bounds__(256) void k_stock_elem(ShardTableN<NT> sh, int tp, int shard, int m,
+                                                    unsigned short *out, int cols) {
+  const long long n = static_cast<long long>(m) * cols;
+  const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+  for (long long e = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
+       e += stride) {
+    const long long row = e / cols;
+    const int col = static_cast<int>(e - row * cols);
+    const int rank = col / shard;
+    const unsigned short *src = reinterpret_cast<const unsigned short *>(sh.p[rank]);
+    out[e] = src[row * shard + (col - rank * shard)];
   }
 }
 
 template <int N>
 using Int = std::integral_constant<int, N>;
 
+// Vectors per lane: 1 or 2 for the mailbox kernels, also 4 for the stock copy.
 template <typename F>
 hipError_t by_vpt(int vpt, F &&f) {
   switch (vpt) {
     case 1: return f(Int<1>{});
     case 2: return f(Int<2>{});
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <typename F>
+hipError_t by_stock_vpt(int vpt, F &&f) {
+  switch (vpt) {
+    case 1: return f(Int<1>{});
+    case 2: return f(Int<2>{});
     case 4: return f(Int<4>{});
-    case 8: return f(Int<8>{});
     default: return hipErrorInvalidValue;
   }
 }
@@ -509,25 +534,11 @@ hipError_t by_table(const ShardTable &sh, int tp, F &&f) {
   return f(sh);
 }
 
+// Calls f with the (push, poll) flavour pair of a launch.
 template <typename F>
-hipError_t by_push(int mode, F &&f) {
-  switch (mode) {
-    case kPushAgent64: return f(Int<kPushAgent64>{});
-    case kPushPlain: return f(Int<kPushPlain>{});
-    case kPushB128Sc1: return f(Int<kPushB128Sc1>{});
-    case kPushB128Sc1Nt: return f(Int<kPushB128Sc1Nt>{});
-    default: return hipErrorInvalidValue;
-  }
-}
-
-template <typename F>
-hipError_t by_poll(int mode, F &&f) {
-  switch (mode) {
-    case kPollAgent64: return f(Int<kPollAgent64>{});
-    case kPollB128Sc1: return f(Int<kPollB128Sc1>{});
-    case kPollB128Sc1Nt: return f(Int<kPollB128Sc1Nt>{});
-    default: return hipErrorInvalidValue;
-  }
+hipError_t by_flavour(int wide, F &&f) {
+  if (wide) return f(Int<kPushAgent64>{}, Int<kPollAgent64>{});
+  return f(Int<kPushB128Sc1>{}, Int<kPollB128Sc1Nt>{});
 }
 
 }  // namespace
@@ -571,13 +582,11 @@ hipError_t launch_fused(const ShardTable &sh, const Geometry &g, const Modes &md
   return by_table(sh, g.tp, [&](const auto &t) {
     constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
     return by_vpt(md.vpt, [&](auto v) {
-      return by_push(md.push, [&](auto pu) {
-        return by_poll(md.poll, [&](auto po) {
-          constexpr int V = decltype(v)::value, PU = decltype(pu)::value, PO = decltype(po)::value;
-          hipLaunchKernelGGL((k_fused<V, PU, PO, NT>), dim3(grid), dim3(block), 0, s, t, g, pa,
-                             box_bytes, out, status, limit, skew, md.rearm_stream);
-          return hipGetLastError();
-        });
+      return by_flavour(md.wide, [&](auto pu, auto po) {
+        constexpr int V = decltype(v)::value, PU = decltype(pu)::value, PO = decltype(po)::value;
+        hipLaunchKernelGGL((k_fused<V, PU, PO, NT>), dim3(grid), dim3(block), 0, s, t, g, pa,
+                           box_bytes, out, status, limit, skew);
+        return hipGetLastError();
       });
     });
   });
@@ -599,20 +608,20 @@ hipError_t launch_collect(const Geometry &g, const Modes &md, const ParityArg &p
                           unsigned box_bytes, const OutRows &out, unsigned *status,
                           unsigned long long limit, int grid, int block, hipStream_t s) {
   return by_vpt(md.vpt, [&](auto v) {
-    return by_poll(md.poll, [&](auto po) {
+    return by_flavour(md.wide, [&](auto, auto po) {
       constexpr int V = decltype(v)::value, PO = decltype(po)::value;
       hipLaunchKernelGGL((k_collect<V, PO>), dim3(grid), dim3(block), 0, s, g, pa, box_bytes, out,
-                         status, limit, md.rearm_stream);
+                         status, limit);
       return hipGetLastError();
     });
   });
 }
 
-hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, u32x4 *out, int grid,
-                        int block, hipStream_t s) {
+hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, const OutRows &out,
+                        int grid, int block, hipStream_t s) {
   return by_table(sh, g.tp, [&](const auto &t) {
     constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
-    return by_vpt(vpt, [&](auto v) {
+    return by_stock_vpt(vpt, [&](auto v) {
       constexpr int V = decltype(v)::value;
       hipLaunchKernelGGL((k_stock<V, NT>), dim3(grid), dim3(block), 0, s, t, g, out);
       return hipGetLastError();
@@ -620,16 +629,24 @@ hipError_t launch_stock(const ShardTable &sh, const Geometry &g, int vpt, u32x4 
   });
 }
 
+hipError_t launch_stock_elem(const ShardTable &sh, int tp, int shard, int m, unsigned short *out,
+                             int cols, int grid, int block, hipStream_t s) {
+  return by_table(sh, tp, [&](const auto &t) {
+    constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
+    hipLaunchKernelGGL((k_stock_elem<NT>), dim3(grid), dim3(block), 0, s, t, tp, shard, m, out,
+                       cols);
+    return hipGetLastError();
+  });
+}
+
 hipError_t fused_blocks_per_cu(const Modes &md, int tp, int block, int *blocks) {
   return by_vpt(md.vpt, [&](auto v) {
-    return by_push(md.push, [&](auto pu) {
-      return by_poll(md.poll, [&](auto po) {
-        constexpr int V = decltype(v)::value, PU = decltype(pu)::value, PO = decltype(po)::value;
-        const void *fn = tp <= kSmallTable
-                             ? reinterpret_cast<const void *>(&k_fused<V, PU, PO, kSmallTable>)
-                             : reinterpret_cast<const void *>(&k_fused<V, PU, PO, HG_MAX_TP>);
-        return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fn, block, 0);
-      });
+    return by_flavour(md.wide, [&](auto pu, auto po) {
+      constexpr int V = decltype(v)::value, PU = decltype(pu)::value, PO = decltype(po)::value;
+      const void *fn = tp <= kSmallTable
+                           ? reinterpret_cast<const void *>(&k_fused<V, PU, PO, kSmallTable>)
+                           : reinterpret_cast<const void *>(&k_fused<V, PU, PO, HG_MAX_TP>);
+      return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks, fn, block, 0);
     });
   });
 }

@@ -54,30 +54,33 @@ def _shard_pointers(shards, tp: int) -> tuple[list[int], int, int, torch.device,
 
 
 def stock_gather(shards: torch.Tensor | Sequence[torch.Tensor], tp: int,
-                 out: torch.Tensor | None = None) -> torch.Tensor:
+                 out: torch.Tensor | None = None, vocab: int | None = None) -> torch.Tensor:
     """The stock gather: rank-order concatenation ``[M, TP*S]``, bytes
     unchanged (the single-device share of an all-gather followed by the copy to
-    ``[M, V]``). The shards must be on a CUDA device. Rows of a multiple of 16
-    bytes (any dtype: the concatenation only moves bytes) run in the library's
-    kernel; other widths take ``torch.cat`` on the device."""
+    ``[M, V]``), of which the library's kernel writes the first ``vocab``
+    columns (default: all). The shards must be on a CUDA device and their rows
+    a whole number of 2-byte units (any dtype: the concatenation only moves
+    bytes)."""
     ptrs, m, s, device, dtype = _shard_pointers(shards, tp)
     if device.type != "cuda":
         raise ValueError(f"shards must be on a CUDA device, got {device}")
+    cols = tp * s if vocab is None else int(vocab)
+    if not 1 <= cols <= tp * s:
+        raise ValueError(f"vocab must lie in 1..{tp * s}, got {cols}")
     if out is None:
-        out = torch.empty((m, tp * s), dtype=dtype, device=device)
-    elif out.dtype != dtype or tuple(out.shape) != (m, tp * s) or not out.is_contiguous():
-        raise ValueError(f"out must be a contiguous {dtype} [{m}, {tp * s}] tensor")
-    row_bytes = s * torch.empty((), dtype=dtype).element_size()
-    if row_bytes % 16:
-        parts = list(shards) if not isinstance(shards, torch.Tensor) else list(shards.unbind(0))
-        torch.cat(parts, dim=1, out=out)
-        return out
+        out = torch.empty((m, cols), dtype=dtype, device=device)
+    elif out.dtype != dtype or tuple(out.shape) != (m, cols) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous {dtype} [{m}, {cols}] tensor")
+    esize = torch.empty((), dtype=dtype).element_size()
+    if (s * esize) % 2 or (cols * esize) % 2:
+        raise ValueError("the stock gather moves 2-byte units: row widths in bytes must be even")
     if m == 0:
         return out
     with torch.cuda.device(device):
-        # the kernel counts the row in BF16 elements (two bytes each)
-        check(lib().hg_stock_gather(tp, row_bytes // 2, pointer_array(ptrs), m,
-                                    ctypes.c_void_p(out.data_ptr()), _stream_handle(device)),
+        # the kernel counts widths in 2-byte units
+        check(lib().hg_stock_gather(tp, s * esize // 2, pointer_array(ptrs), m,
+                                    ctypes.c_void_p(out.data_ptr()), cols * esize // 2,
+                                    _stream_handle(device)),
               "hg_stock_gather")
     return out
 
@@ -100,7 +103,7 @@ def _weight_pointers(w, tp: int, shard: int, hidden: int) -> list[int]:
 
 
 def lmhead(x: torch.Tensor, w, tp: int, shard: int,
-           shards_out: torch.Tensor | None = None, variant: int = 0) -> torch.Tensor:
+           shards_out: torch.Tensor | None = None) -> torch.Tensor:
     """The lm_head shard product ``[TP, M, S] = X @ W_r^T`` per rank (BF16 in,
     fp32 accumulate, BF16 out), in the library's MFMA kernel."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or not x.is_contiguous():
@@ -116,7 +119,7 @@ def lmhead(x: torch.Tensor, w, tp: int, shard: int,
     op = [shards_out.data_ptr() + r * step for r in range(tp)]
     with torch.cuda.device(x.device):
         check(lib().hg_lmhead(tp, shard, ctypes.c_void_p(x.data_ptr()), pointer_array(wp), hidden, m,
-                              pointer_array(op), int(variant), _stream_handle(x.device)), "hg_lmhead")
+                              pointer_array(op), _stream_handle(x.device)), "hg_lmhead")
     return shards_out
 
 
@@ -178,16 +181,10 @@ class HeadGather:
         return out
 
     def _stock(self, shards, s: int, out: torch.Tensor | None) -> torch.Tensor:
-        """The stock gather; shards of this context's width are sliced to the
-        vocabulary like a served call."""
-        if self.vocab == self.width or s != self.shard:
-            return stock_gather(shards, self.tp, out)
-        full = stock_gather(shards, self.tp)
-        part = full[:, : self.vocab]
-        if out is None:
-            return part.contiguous()
-        out.copy_(part)
-        return out
+        """The stock gather; shards of this context's width keep the
+        vocabulary's columns like a served call (the library's stock kernel
+        writes only those)."""
+        return stock_gather(shards, self.tp, out, self.vocab if s == self.shard else None)
 
     def __call__(self, shards, out: torch.Tensor | None = None) -> torch.Tensor:
         """Gather ``[M, S]`` x TP -> ``[M, vocab]``. Served calls run the fused
@@ -301,15 +298,6 @@ class HeadGather:
         if rc == _lib.HG_ETIMEOUT:
             return rc
         return check(rc, "hg_poll_status")
-
-    def set_tuning(self, knob: int, value: int) -> None:
-        with torch.cuda.device(self.device):
-            check(lib().hg_set_tuning(self._h, knob, int(value)), "hg_set_tuning")
-
-    def get_tuning(self, knob: int) -> int:
-        v = ctypes.c_int()
-        check(lib().hg_get_tuning(self._h, knob, ctypes.byref(v)), "hg_get_tuning")
-        return v.value
 
     def fused_grid_limit(self, m: int) -> int:
         with torch.cuda.device(self.device):
