@@ -63,6 +63,7 @@ extern "C" {
 #define HG_EHIP (-3)   /* a HIP runtime call failed (see hg_last_error_detail)  */
 #define HG_ETIMEOUT (-4) /* a bounded poll gave up (reported by hg_poll_status)  */
 #define HG_ESTATE (-5) /* split-variant call out of order                       */
+#define HG_ESIZE (-6)  /* beyond the static scratch buffer (hg_gather_static)   */
 
 typedef struct hg_ctx hg_ctx;
 
@@ -282,6 +283,35 @@ int hg_set_poll_limit(hg_ctx *h, unsigned long long spins);
  * HG_EINVAL if the stream is capturing. The reporting side of the bounded
  * poll (hg_set_poll_limit); not on the pages. */
 int hg_poll_status(hg_ctx *h, void *stream);
+
+/*
+ * The fused gather without allocation, for callers that cannot call
+ * hipMalloc: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation. It computes what hg_gather computes for a context of
+ * (tp, shard, cap >= m) with device-side parity, and writes `out`
+ * ([m][tp*shard] BF16, whole rows) exactly as hg_gather does; it needs no
+ * context. Its mailbox (two parities of HG_STATIC_PARITY_BYTES each), parity
+ * slots and poll-timeout counter live in a static device array of the
+ * library, one per device, resolved on the first call on each device (which
+ * arms the mailbox on `stream`) and kept until the process ends. No call
+ * allocates device or host memory.
+ *
+ * Limits: m * tp * shard * 2 <= HG_STATIC_PARITY_BYTES (a larger call returns
+ * HG_ESIZE and enqueues nothing); tp in [2, HG_MAX_TP], shard >= 8 and
+ * shard % 8 == 0 (else HG_EINVAL); m == 0 is declined (HG_EDECLINE), m < 0 is
+ * HG_EINVAL; shards and out 16-byte aligned, out overlapping no shard. The
+ * first call on a device must not be made under graph capture (HG_ESTATE);
+ * later calls may be captured, and replays alternate the parity.
+ *
+ * Every call on one device shares that device's scratch array, which keeps
+ * the previous call's state (the parity, an all-sentinel mailbox): issue all
+ * calls on a device from one host thread and on one stream; calls that
+ * overlap on one device (two streams, two threads) race. A poll that gives up
+ * after 2^24 re-reads is counted in the scratch array and not reported.
+ */
+#define HG_STATIC_PARITY_BYTES (8u << 20)
+int hg_gather_static(int tp, int shard, const void *const *shards, int m, void *out,
+                     void *stream);
 
 /* Workgroups the fused kernel of an m-row call may keep resident at once on
  * the context's device (its grid never exceeds this, so every workgroup whose

@@ -95,10 +95,27 @@ def test_stock_gather_argument_checks():
     assert lib.hg_stock_gather(2, 8, overlap, 1, out, 16, None) == _lib.HG_EINVAL
 
 
+def test_static_gather_host_checks():
+    # sizes are refused before any device call (hg_gather_static's limit is
+    # HG_STATIC_PARITY_BYTES per parity: 25 rows of V = 163840)
+    lib = _lib.lib()
+    ptrs = _lib.pointer_array([16] * 8)
+    out = ctypes.c_void_p(1 << 30)
+    assert lib.hg_gather_static(8, 20480, ptrs, 26, out, None) == _lib.HG_ESIZE
+    assert b"static" in lib.hg_last_error_detail()
+    assert lib.hg_gather_static(8, 20480, ptrs, 1 << 30, out, None) == _lib.HG_ESIZE
+    assert lib.hg_gather_static(1, 20480, ptrs, 1, out, None) == _lib.HG_EINVAL
+    assert lib.hg_gather_static(8, 12, ptrs, 1, out, None) == _lib.HG_EINVAL
+    assert lib.hg_gather_static(8, 20480, ptrs, -1, out, None) == _lib.HG_EINVAL
+    assert lib.hg_gather_static(8, 20480, ptrs, 0, out, None) == _lib.HG_EDECLINE
+    assert lib.hg_gather_static(8, 20480, None, 1, out, None) == _lib.HG_EINVAL
+    assert lib.hg_strerror(_lib.HG_ESIZE) == b"request exceeds the static scratch buffer"
+
+
 def test_status_strings():
     lib = _lib.lib()
     for code in (_lib.HG_OK, _lib.HG_EDECLINE, _lib.HG_EINVAL, _lib.HG_ENOMEM, _lib.HG_EHIP,
-                 _lib.HG_ETIMEOUT, _lib.HG_ESTATE, 1234):
+                 _lib.HG_ETIMEOUT, _lib.HG_ESTATE, _lib.HG_ESIZE, 1234):
         assert lib.hg_strerror(code)
     assert lib.hg_last_error_detail() is not None
 

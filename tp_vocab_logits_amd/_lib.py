@@ -22,6 +22,8 @@ HG_ENOMEM = -2
 HG_EHIP = -3
 HG_ETIMEOUT = -4
 HG_ESTATE = -5
+HG_ESIZE = -6
+HG_STATIC_PARITY_BYTES = 8 << 20
 HG_MAX_TP = 64
 
 _vp = ctypes.c_void_p
@@ -51,6 +53,7 @@ SIGNATURES = {
     "hg_set_poll_limit": (_i, [_ctxp, _ull]),
     "hg_poll_status": (_i, [_ctxp, _vp]),
     "hg_fused_grid_limit": (_i, [_ctxp, _i]),
+    "hg_gather_static": (_i, [_i, _i, ctypes.POINTER(_vp), _i, _vp, _vp]),
     "hg_strerror": (ctypes.c_char_p, [_i]),
     "hg_last_error_detail": (ctypes.c_char_p, []),
 }

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libhg.so")
-SOURCES = ["hg_api.cpp", "hg_kernels.hip", "hg_lmhead.hip"]
+SOURCES = ["hg_api.cpp", "hg_kernels.hip", "hg_lmhead.hip", "hg_static.hip"]
 ARCH = "gfx950"
 FASTCALL = os.path.join(PKG, "_hgcall" + sysconfig.get_config_var("EXT_SUFFIX"))
 REF_LIB = os.path.join(PKG, "libhgref.so")  # the benchmark's reference streaming kernel

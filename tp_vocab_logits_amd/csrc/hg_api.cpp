@@ -41,32 +41,39 @@ int hip_fail(hipError_t e, const char *where) {
   return HG_EHIP;
 }
 
+}  // namespace
+
+namespace hg {
+
+int record_hip_error(hipError_t e, const char *where) { return hip_fail(e, where); }
+
+void record_error(const char *what) { snprintf(g_last_error, sizeof g_last_error, "%s", what); }
+
+}  // namespace hg
+
+namespace {
+
 #define HIP_TRY(expr)                                 \
   do {                                                \
     hipError_t e_ = (expr);                           \
     if (e_ != hipSuccess) return hip_fail(e_, #expr); \
   } while (0)
 
-// Launch shape, chosen by sweeps on MI355X (TP=8, V=163840, M = 1..256):
-// 128-bit agent-coherent pushes and polls move the M=256 gather at about 85 %
-// of HBM peak against about 60 % for pairs of 64-bit atomics; four resident
+// Launch shape (hg::kBlock, hg::kGridPerCu, hg::kPollSkew, hg::mailbox_vpt),
+// chosen by sweeps on MI355X (TP=8, V=163840, M = 1..256): 128-bit
+// agent-coherent pushes and polls move the M=256 gather at about 85 % of HBM
+// peak against about 60 % for pairs of 64-bit atomics; four resident
 // 256-thread workgroups per CU beat the full co-resident grid; a poll skew of
 // 1 keeps every poll on data pushed by a workgroup on another XCD, within
-// about 0.1 us per M=1 call of self-polling.
-constexpr int kBlock = 256;
-constexpr int kGridPerCu = 4;
-constexpr int kPollSkew = 1;
-
-// Vectors per lane for a launch moving `vectors` 16-byte vectors per phase:
-// one while the call is small (latency: spread it over many waves), two when
-// it is large (more bytes in flight per lane). Measured under graph replay
-// with 256-thread workgroups (TP=8, V=163840): M=4 takes 4.22 us with one
-// against 4.48 with two; M=64 17.1 us with two against 18.4 with one and
-// 17.4 with four; M=256 61.8 us with two against 63.0 with four.
-int mailbox_vpt(long long vectors, int cus) {
-  const long long lanes = static_cast<long long>(cus) * 256;
-  return vectors <= 4 * lanes ? 1 : 2;
-}
+// about 0.1 us per M=1 call of self-polling. One vector per lane while the
+// call is small (latency: spread it over many waves), two when it is large
+// (more bytes in flight per lane); measured under graph replay (TP=8,
+// V=163840): M=4 takes 4.22 us with one against 4.48 with two; M=64 17.1 us
+// with two against 18.4 with one and 17.4 with four; M=256 61.8 us with two
+// against 63.0 with four.
+using hg::kBlock;
+using hg::kPollSkew;
+using hg::mailbox_vpt;
 
 // The stock concatenation (a plain copy, no polling) keeps its own
 // thresholds, up to four vectors per lane.
@@ -188,22 +195,12 @@ int load_shards(int tp, int shard, const void *const *shards, int m, unsigned lo
   return HG_OK;
 }
 
-// Workgroups of a fused launch: one per tile of 4 chunks, at most kGridPerCu
-// per CU and never more than can be resident at once (every workgroup whose
-// pushes are awaited must be running), nor more waves than parity slots.
 int fused_grid(hg_ctx *h, const hg::Modes &md, const Geometry &g, int *grid) {
-  const int waves = kBlock / 64;
-  const long long tiles = (static_cast<long long>(g.chunks) + waves - 1) / waves;
   int per_cu = 0;
   const int rc = fused_per_cu(h, md, &per_cu);
   if (rc != HG_OK) return rc;
-  long long lim = static_cast<long long>(per_cu) * h->cus;
-  const long long want = static_cast<long long>(kGridPerCu) * h->cus;
-  if (want < lim) lim = want;
-  if (lim > hg::kParitySlots / waves) lim = hg::kParitySlots / waves;  // one slot per wave
-  if (lim < 1) return HG_EINVAL;
-  *grid = static_cast<int>(tiles < lim ? tiles : lim);
-  return HG_OK;
+  *grid = hg::fused_launch_grid(g.chunks, per_cu, h->cus);
+  return *grid >= 1 ? HG_OK : HG_EINVAL;
 }
 
 int split_grid(const hg_ctx *h, const Geometry &g, int block) {
@@ -627,6 +624,7 @@ HG_API const char *hg_strerror(int code) {
     case HG_EHIP: return "HIP runtime error";
     case HG_ETIMEOUT: return "a bounded mailbox poll gave up";
     case HG_ESTATE: return "split push/collect called out of order";
+    case HG_ESIZE: return "request exceeds the static scratch buffer";
     default: return "unknown status";
   }
 }

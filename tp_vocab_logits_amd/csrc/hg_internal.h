@@ -170,4 +170,36 @@ hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &sh
 // Resident workgroups per CU of the fused kernel variant at a block size.
 hipError_t fused_blocks_per_cu(const Modes &md, int tp, int block, int *blocks);
 
+// Launch shape of the mailbox kernels: 256-thread workgroups, at most four
+// resident per CU, one vector per lane while a phase moves at most four
+// vectors per lane slot of the device, two beyond.
+constexpr int kBlock = 256;
+constexpr int kGridPerCu = 4;
+constexpr int kPollSkew = 1;
+
+inline int mailbox_vpt(long long vectors, int cus) {
+  const long long lanes = static_cast<long long>(cus) * kBlock;
+  return vectors <= 4 * lanes ? 1 : 2;
+}
+
+// Workgroups of a fused launch over `chunks` chunks: one per tile of
+// kBlock/64 chunks, at most kGridPerCu per CU and never more than can be
+// resident at once (every workgroup whose pushes are awaited must be
+// running), nor more waves than parity slots. 0 if nothing fits.
+inline int fused_launch_grid(long long chunks, int per_cu, int cus) {
+  const int waves = kBlock / 64;
+  const long long tiles = (chunks + waves - 1) / waves;
+  long long lim = static_cast<long long>(per_cu) * cus;
+  const long long want = static_cast<long long>(kGridPerCu) * cus;
+  if (want < lim) lim = want;
+  if (lim > kParitySlots / waves) lim = kParitySlots / waves;  // one slot per wave
+  if (lim < 1) return 0;
+  return static_cast<int>(tiles < lim ? tiles : lim);
+}
+
+// The library's last-error text (hg_last_error_detail): a failed HIP call
+// (returns HG_EHIP), or a plain message.
+int record_hip_error(hipError_t e, const char *where);
+void record_error(const char *what);
+
 }  // namespace hg
