@@ -18,6 +18,8 @@
 // and each 32 x 32 output block is one chain of MFMAs over K in increasing
 // order: the result bits do not depend on the tiling around it.
 
+#include <type_traits>
+
 #include "hg_internal.h"
 
 namespace hg {
@@ -59,169 +61,244 @@ __device__ __forceinline__ void wait_vm() {
 }
 
 // 256 x 320 output tiles: 163840 columns make 512 tiles, two full rounds on
-// 256 CUs. Eight waves of 64 rows x 160 columns (2 x 5 MFMA blocks, 160
-// accumulator registers). 64-wide K steps, two LDS stages of [256 X rows +
-// 320 weight rows] x 128 bytes (72 KB each), filled by buffer loads straight
-// into LDS (buffer_load_dwordx4 ... lds) one step ahead; a wave's load
-// instruction fills 8 rows, lane-major, each lane loading the K segment that
-// the swizzle puts at its slot. X: one buffer resource from the tile's first
-// row. Weights: with ONE_RANK (shard a multiple of 320, so no tile straddles
-// two ranks) one resource from the tile's first row; otherwise one per load
-// instruction, from the first of its 8 rows (all of one rank, as
-// shard % 32 == 0).
-template <int NT, bool ONE_RANK, bool PUSH, bool KEEP>
-__global__ __launch_bounds__(512) void k_lmhead_n320b(const u32x4 *x, ShardTableN<NT> w,
-                                                      OutTableN<NT> shards_out, ParityArg pa,
-                                                      int m, int hidden, int shard, int vocab) {
+// 256 CUs. Eight waves; wave w owns rows 32w .. 32w+31 of the tile and all
+// 320 columns: ten 32 x 32 blocks of v_mfma_f32_32x32x16_bf16, 160
+// accumulator registers.
+//
+// Both operands arrive by buffer loads straight into LDS (buffer_load_dwordx4
+// ... lds), each instruction filling 8 rows of 128 bytes (one 64-wide K step)
+// lane-major, every lane loading the K segment that the swizzle puts at its
+// slot, so the global side is 8 full 128-byte lines per instruction.
+//  - Weights (shared by all waves, streamed once from HBM): ST stages of
+//    320 rows (40 KB each), loaded ST-1 steps ahead.
+//  - X (served from L2: every column tile re-reads it): each wave's 32 rows
+//    are private to it, so each wave has its own 4 KB region, loaded one step
+//    ahead and read back into registers right after the step's barrier,
+//    before the region is refilled.
+// Weights: with ONE_RANK (shard a multiple of 320, so no tile straddles two
+// ranks) one buffer resource from the tile's first row; otherwise one per
+// load instruction, from the first row of its group of 8 (never straddling
+// two ranks, as shard % 32 == 0).
+//
+// Rows past m (X) or past the vocabulary (weights) lie beyond their buffer
+// resource's size, so the hardware's range check makes them read as zero.
+// K segments past `hidden` (the last step of a hidden size that is not a
+// multiple of 64) read the next row's data, or zero past the resource, and
+// are cleared before use: in LDS for the weights, in registers for X.
+//
+// Step kb: wait for X(kb) and the weights of step kb; barrier; read X(kb)
+// into registers; issue X(kb+1), then the weights of step kb+ST-1; multiply.
+// The loads complete in issue order, so at the top of step kb one wait for
+// "all but the newest weight loads" covers X(kb) and W(kb) while ST-2 steps of
+// weights stay in flight across it.
+template <int NT, bool ONE_RANK, bool PUSH, bool KEEP, int ST, bool LATE>
+__global__ __launch_bounds__(512) void k_lmhead(const u32x4 *x, ShardTableN<NT> w,
+                                                OutTableN<NT> shards_out, ParityArg pa, int m,
+                                                int hidden, int shard, int vocab) {
+  static_assert(ST >= 3, "the weights run at least two steps ahead");
+  constexpr int NW = 8;
   constexpr int KS = 64;
   constexpr int kTN = 320;
   constexpr int kRowBytes = 128;
-  constexpr int kSlots = 8;
-  constexpr int kXPart = kTM * kRowBytes;           // 32 KB
-  constexpr int kStage = (kTM + kTN) * kRowBytes;   // 72 KB
-  constexpr int kXInst = 4, kWInst = 5;             // per wave per step
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kStage];
+  constexpr int kSlots = 8;                   // 16-byte K segments per row and step
+  constexpr int kStage = kTN * kRowBytes;     // 40 KB
+  constexpr int kXRegion = 32 * kRowBytes;    // 4 KB per wave
+  constexpr int kWInst = kTN / 8 / NW;        // weight load instructions per wave and step
+  constexpr int kXInst = 4;                   // X load instructions per wave and step
+  constexpr int kBlocks = kTN / 32;           // column blocks
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[ST * kStage + NW * kXRegion];
 
   const int tid = static_cast<int>(threadIdx.x);
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int mq = wave & 3;   // 64-row quarter of the tile
-  const int nh = wave >> 2;  // 160-column half of the tile
   const int half = lane >> 5;
   const int l32 = lane & 31;
   const int n0 = static_cast<int>(blockIdx.x) * kTN;
   const int m0 = static_cast<int>(blockIdx.y) * kTM;
   const int hv = hidden >> 3;
   const int steps = (hidden + KS - 1) / KS;
-
-  // Instruction q of wave w fills rows 8*(8q+w) .. +8 of an operand. A lane
-  // whose row is out of range (or whose K segment is past `hidden`) loads
-  // offset 0 instead; its slot is cleared before use.
   const int lrow = lane >> 3, lslot = lane & 7;
+  unsigned char *xreg = lds + ST * kStage + wave * kXRegion;
+
+  // MFMA j of a step takes the lane's K segment 4*(j/2) + 2*half + j%2, of
+  // X row 32*wave + l32 and weight row 32*cb + l32. Both are read from rows
+  // whose swizzle is (l32 ^ (l32 >> 3)) & 7, with 4 more for odd cb (row
+  // 32*cb + l32 has (row >> 3) & 7 = 4*(cb & 1) + (l32 >> 3)): per j one X
+  // offset and two weight offsets, the block's 4096*cb an immediate offset.
+  const int s0 = (l32 ^ (l32 >> 3)) & 7;
+  int xseg[4], xoff[4], boff[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    xseg[j] = 4 * (j >> 1) + 2 * half + (j & 1);
+    xoff[j] = l32 * kRowBytes + ((xseg[j] ^ s0) << 4);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) boff[j][p] = l32 * kRowBytes + ((xseg[j] ^ s0 ^ (4 * p)) << 4);
+  }
+
+  // X loads: instruction q fills rows 8q .. 8q+7 of the wave's region; lane
+  // (lrow, lslot) loads row 8q + lrow's segment lslot ^ swizzle(8q + lrow) =
+  // lslot ^ ((lrow ^ q) & 7). The wave's and the instruction's rows are a
+  // uniform part of the offset.
   const int xrows = m - m0 < kTM ? m - m0 : kTM;
+  const bool computes = 32 * wave < xrows;  // wave-uniform: a row of this wave is below m
   const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<u32x4 *>(x + static_cast<long long>(m0) * hv), 0, xrows * hidden * 2,
       kRawBufferWord3);
-  __amdgpu_buffer_rsrc_t wres[kWInst];
-  int xoff[kXInst], woff[kWInst], xseg[kXInst], wseg[kWInst];
-  bool xok[kXInst], wok[kWInst];
+  int xvo[kXInst], xslot[kXInst];
 #pragma unroll
   for (int q = 0; q < kXInst; ++q) {
-    const int row = 8 * (8 * q + wave) + lrow;  // 0..255
-    xseg[q] = lslot ^ dswz<64>(row);
-    xok[q] = row < xrows;
-    xoff[q] = row * hv * 16;
+    xslot[q] = lslot ^ ((lrow ^ q) & 7);
+    xvo[q] = lrow * hv * 16 + xslot[q] * 16;
   }
+
+  // Weight loads: instruction q of wave w fills stage rows 8*g .. 8*g+7,
+  // g = 8q + w, so (g & 7) = w and one lane offset serves every instruction;
+  // the row group's part of the offset is uniform.
+  const int wslot = lslot ^ ((lrow ^ wave) & 7);
+  const int wvo = lrow * hv * 16 + wslot * 16;
+  __amdgpu_buffer_rsrc_t wres0;
   if constexpr (ONE_RANK) {
     const int r = n0 / shard;
     const int trows = vocab - n0 < kTN ? vocab - n0 : kTN;
-    wres[0] = __builtin_amdgcn_make_buffer_rsrc(
+    wres0 = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<u32x4 *>(w.p[r] + static_cast<long long>(n0 - r * shard) * hv), 0,
         trows * hidden * 2, kRawBufferWord3);
   }
-#pragma unroll
-  for (int q = 0; q < kWInst; ++q) {
-    const int row = 8 * (8 * q + wave) + lrow;  // 0..319
-    wseg[q] = lslot ^ dswz<64>(row);
-    wok[q] = n0 + row < vocab;
+  auto wsrc = [&](int q, int *row_off) __attribute__((always_inline)) {
+    const int g = NW * q + wave;
     if constexpr (ONE_RANK) {
-      woff[q] = row * hv * 16;
+      *row_off = 8 * g * hv * 16;
+      return wres0;
     } else {
-      const int nfirst = __builtin_amdgcn_readfirstlane(n0 + 8 * (8 * q + wave));
+      const int nfirst = n0 + 8 * g;
       const int r = nfirst < vocab ? nfirst / shard : 0;
-      const int s0 = nfirst < vocab ? nfirst - r * shard : 0;
-      const int grows = nfirst < vocab ? (vocab - nfirst < 8 ? vocab - nfirst : 8) : 1;
-      wres[q] = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<u32x4 *>(w.p[r] + static_cast<long long>(s0) * hv), 0, grows * hidden * 2,
+      const int s0r = nfirst < vocab ? nfirst - r * shard : 0;
+      const int grows = nfirst < vocab ? (vocab - nfirst < 8 ? vocab - nfirst : 8) : 0;
+      *row_off = 0;
+      return __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<u32x4 *>(w.p[r] + static_cast<long long>(s0r) * hv), 0, grows * hidden * 2,
           kRawBufferWord3);
-      woff[q] = lrow * hv * 16;
-    }
-  }
-  // X load instructions whose 8 rows all lie past m are not issued: rows past
-  // m only ever reach output rows that are not stored, so their LDS slots may
-  // hold anything (likewise weight rows past the vocabulary).
-  bool xinst[kXInst];
-#pragma unroll
-  for (int q = 0; q < kXInst; ++q) xinst[q] = 8 * (8 * q + wave) < xrows;  // wave-uniform
-  auto issue = [&](int kb) {
-    unsigned char *st = lds + (kb & 1) * kStage;
-#pragma unroll
-    for (int q = 0; q < kXInst; ++q) {
-      if (!xinst[q]) continue;
-      const int kv = kb * kSlots + xseg[q];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          xres, (__attribute__((address_space(3))) void *)(st + 8 * (8 * q + wave) * kRowBytes),
-          16, xok[q] && kv < hv ? xoff[q] + kv * 16 : 0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int q = 0; q < kWInst; ++q) {
-      const int kv = kb * kSlots + wseg[q];
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wres[ONE_RANK ? 0 : q],
-          (__attribute__((address_space(3))) void *)(st + kXPart + 8 * (8 * q + wave) * kRowBytes),
-          16, wok[q] && kv < hv ? woff[q] + kv * 16 : 0, 0, 0, kPolicyNt);
     }
   };
 
-  f32x16 acc[2][5];
+  // Loads of step kb (the step's K offset is part of the scalar offset).
+  auto issue_w = [&](int kb) __attribute__((always_inline)) {
+    unsigned char *st = lds + (kb % ST) * kStage;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int q = 0; q < kWInst; ++q) {
+      int row_off = 0;
+      const __amdgpu_buffer_rsrc_t rs = wsrc(q, &row_off);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void *)(st + 8 * (NW * q + wave) * kRowBytes), 16,
+          wvo, row_off + kb * kRowBytes, 0, kPolicyNt);
+    }
+  };
+  auto issue_x = [&](int kb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int cb = 0; cb < 5; ++cb) acc[i][cb] = f32x16{};
+    for (int q = 0; q < kXInst; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          xres, (__attribute__((address_space(3))) void *)(xreg + 8 * q * kRowBytes), 16, xvo[q],
+          (32 * wave + 8 * q) * hv * 16 + kb * kRowBytes, 0, 0);
+  };
 
-  // Only a K segment past `hidden` must read as zero: it meets real data in
-  // the other operand. Such slots (loaded from offset 0) are cleared.
+  f32x16 acc[kBlocks];
+#pragma unroll
+  for (int cb = 0; cb < kBlocks; ++cb) acc[cb] = f32x16{};
+
   const bool ktail = hidden % KS != 0;
-  // A wave whose 64 rows all lie at or past m computes nothing (wave-uniform):
-  // at small m most waves only stream loads.
-  const bool blk0 = m0 + 64 * mq < m;
-  issue(0);
-  for (int kb = 0; kb < steps; ++kb) {
-    wait_vm<0>();  // this wave's loads of step kb (nothing newer is in flight)
+
+  // One K step. In the steady state (MAIN) the step always issues X(kb+1)
+  // and the weights of step kb+ST-1, so the compiler's wait counts follow one
+  // straight path; the last ST-1 steps (and a wave with no row below m) take
+  // the general form, which waits for everything outstanding.
+  auto step = [&](auto main, auto comp, int kb) __attribute__((always_inline)) {
+    constexpr bool MAIN = decltype(main)::value, COMP = decltype(comp)::value;
+    if constexpr (MAIN)
+      wait_vm<kWInst>();  // X(kb) and every older weight load have landed
+    else
+      wait_vm<0>();
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     __asm__ __volatile__("" ::: "memory");
-    unsigned char *sx = lds + (kb & 1) * kStage;
-    unsigned char *sw = sx + kXPart;
-    if (ktail && (kb + 1) * kSlots > hv) {
+    unsigned char *sw = lds + (kb % ST) * kStage;
+    bf16x8 xa[4];
+    if constexpr (COMP) {
 #pragma unroll
-      for (int q = 0; q < kXInst; ++q) {
-        const int kv = kb * kSlots + xseg[q];
-        if (xinst[q] && kv >= hv)
-          *reinterpret_cast<u32x4 *>(sx + (8 * (8 * q + wave) + lrow) * kRowBytes + lslot * 16) =
-              u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int q = 0; q < kWInst; ++q) {
-        const int kv = kb * kSlots + wseg[q];
-        if (kv >= hv)
-          *reinterpret_cast<u32x4 *>(sw + (8 * (8 * q + wave) + lrow) * kRowBytes + lslot * 16) =
-              u32x4{0u, 0u, 0u, 0u};
-      }
-      __syncthreads();
+      for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const bf16x8 *>(xreg + xoff[j]);
     }
-    if (kb + 1 < steps) issue(kb + 1);
-    if (!blk0) continue;  // no row of this wave's 64 below m: loads only
+    if constexpr (!MAIN) {
+      if (ktail && kb == steps - 1) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // K segment of this lane for MFMA j: 32-wide slice j/2, half, j%2.
-      const int g = 4 * (j >> 1) + 2 * half + (j & 1);
-      bf16x8 a[2];
+        for (int q = 0; q < kWInst; ++q)
+          if (kb * kSlots + wslot >= hv)
+            *reinterpret_cast<u32x4 *>(sw + (8 * (NW * q + wave) + lrow) * kRowBytes +
+                                       lslot * 16) = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (COMP) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int row = 64 * mq + 32 * i + l32;
-        a[i] = *reinterpret_cast<const bf16x8 *>(sx + row * kRowBytes + ((g ^ dswz<64>(row)) << 4));
-      }
-#pragma unroll
-      for (int cb = 0; cb < 5; ++cb) {
-        const int row = 160 * nh + 32 * cb + l32;
-        const bf16x8 b =
-            *reinterpret_cast<const bf16x8 *>(sw + row * kRowBytes + ((g ^ dswz<64>(row)) << 4));
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          acc[i][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, acc[i][cb], 0, 0, 0);
+          for (int j = 0; j < 4; ++j)
+            if (kb * kSlots + xseg[j] >= hv) xa[j] = bf16x8{};
+        }
+        __syncthreads();
       }
     }
+    // X(kb+1) may only refill the region once the X reads above have
+    // returned (lgkmcnt(0)), and it goes out before the weights so that the
+    // next step's single wait covers it. With LATE (most of the tile's rows
+    // computing) the loads go out after the MFMAs of the first K slice, so
+    // that the X reads return under them; with few rows they go out at once,
+    // as the weight stream is then the whole cost.
+    auto loads = [&]() __attribute__((always_inline)) {
+      if constexpr (COMP) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): X(kb) is in registers
+        __asm__ __volatile__("" ::: "memory");
+      }
+      if constexpr (MAIN) {
+        if constexpr (COMP) issue_x(kb + 1);
+        issue_w(kb + ST - 1);
+      } else {
+        if (COMP && kb + 1 < steps) issue_x(kb + 1);
+        if (kb + ST - 1 < steps) issue_w(kb + ST - 1);
+      }
+      __asm__ __volatile__("" ::: "memory");
+    };
+    if constexpr (COMP && !LATE) loads();
+    if constexpr (COMP) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int cb = 0; cb < kBlocks; ++cb) {
+          const bf16x8 b = *reinterpret_cast<const bf16x8 *>(sw + boff[j][cb & 1] +
+                                                             cb * 32 * kRowBytes);
+          acc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xa[j], b, acc[cb], 0, 0, 0);
+        }
+        if (LATE && j == 0) loads();
+      }
+    } else {
+      loads();
+    }
+  };
+
+  // Steps 0 .. nmain-1 are steady-state steps, the rest general ones.
+  const int nmain = steps > ST - 1 ? steps - (ST - 1) : 0;
+  auto run = [&](auto comp) __attribute__((always_inline)) {
+    constexpr bool COMP = decltype(comp)::value;
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    if constexpr (COMP) issue_x(0);
+#pragma unroll
+    for (int s = 0; s < ST - 1; ++s)
+      if (s < steps) issue_w(s);
+    // (X of step 0 goes out before the weights of steps 0 .. ST-2, so the
+    // first wait covers it.)
+    int kb = 0;
+    for (; kb < nmain; ++kb) step(T{}, comp, kb);
+    for (; kb < steps; ++kb) step(F{}, comp, kb);
+  };
+  if (computes) {
+    run(std::integral_constant<bool, true>{});
+  } else {
+    run(std::integral_constant<bool, false>{});  // no row of this wave below m: loads only
+    return;
   }
 
   const bool even = (l32 & 1) == 0;
@@ -230,65 +307,80 @@ __global__ __launch_bounds__(512) void k_lmhead_n320b(const u32x4 *x, ShardTable
   uint32_t *box = PUSH ? reinterpret_cast<uint32_t *>(pa.box + launch_parity(pa) * pa.stride)
                        : nullptr;
 #pragma unroll
-  for (int cb = 0; cb < 5; ++cb) {
-    const int c0 = n0 + 160 * nh + 32 * cb;
+  for (int cb = 0; cb < kBlocks; ++cb) {
+    const int c0 = n0 + 32 * cb;
     if (c0 >= vocab) continue;
     const int r = c0 / shard;
     const int s_even = c0 - r * shard + (l32 & ~1);
     const int wcol = s_even >> 1;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int q = 0; q < 4; ++q) {
+      uint32_t b[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t b[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) b[t] = bf16_bits(acc[i][cb][4 * q + t]);
-        const uint32_t send = even ? (b[1] | (b[3] << 16)) : (b[0] | (b[2] << 16));
-        const uint32_t recv = swap_adjacent(send);
-        const uint32_t w0 = even ? (b[0] | (recv << 16)) : ((recv & 0xFFFFu) | (b[1] << 16));
-        const uint32_t w1 = even ? (b[2] | (recv & 0xFFFF0000u)) : ((recv >> 16) | (b[3] << 16));
-        const int rbase = m0 + 64 * mq + 32 * i + 8 * q + 4 * half;
-        const int row0 = rbase + (even ? 0 : 1);
-        const int row1 = rbase + (even ? 2 : 3);
-        if (row0 < m) {
-          if (KEEP) shards_out.p[r][static_cast<long long>(row0) * words_per_shard_row + wcol] = w0;
-          if (PUSH)
-            box[static_cast<long long>(row0) * words_per_row + (r * shard >> 1) + wcol] =
-                w0 == kSentinel ? 0u : w0;
-        }
-        if (row1 < m) {
-          if (KEEP) shards_out.p[r][static_cast<long long>(row1) * words_per_shard_row + wcol] = w1;
-          if (PUSH)
-            box[static_cast<long long>(row1) * words_per_row + (r * shard >> 1) + wcol] =
-                w1 == kSentinel ? 0u : w1;
-        }
+      for (int t = 0; t < 4; ++t) b[t] = bf16_bits(acc[cb][4 * q + t]);
+      // lanes 2c and 2c+1 hold columns 2c and 2c+1 of rows rbase .. rbase+3;
+      // one swap gives each the words (two adjacent columns) of two rows
+      const uint32_t send = even ? (b[1] | (b[3] << 16)) : (b[0] | (b[2] << 16));
+      const uint32_t recv = swap_adjacent(send);
+      const uint32_t w0 = even ? (b[0] | (recv << 16)) : ((recv & 0xFFFFu) | (b[1] << 16));
+      const uint32_t w1 = even ? (b[2] | (recv & 0xFFFF0000u)) : ((recv >> 16) | (b[3] << 16));
+      const int rbase = m0 + 32 * wave + 8 * q + 4 * half;
+      const int row0 = rbase + (even ? 0 : 1);
+      const int row1 = rbase + (even ? 2 : 3);
+      if (row0 < m) {
+        if (KEEP) shards_out.p[r][static_cast<long long>(row0) * words_per_shard_row + wcol] = w0;
+        if (PUSH)
+          box[static_cast<long long>(row0) * words_per_row + (r * shard >> 1) + wcol] =
+              w0 == kSentinel ? 0u : w0;
+      }
+      if (row1 < m) {
+        if (KEEP) shards_out.p[r][static_cast<long long>(row1) * words_per_shard_row + wcol] = w1;
+        if (PUSH)
+          box[static_cast<long long>(row1) * words_per_row + (r * shard >> 1) + wcol] =
+              w1 == kSentinel ? 0u : w1;
       }
     }
   }
 }
 
+#ifndef HG_LMHEAD_STAGES
+#define HG_LMHEAD_STAGES 3
+#endif
+constexpr int kStages = HG_LMHEAD_STAGES;
+#ifndef HG_LMHEAD_LATE_ROWS
+#define HG_LMHEAD_LATE_ROWS 128
+#endif
+constexpr int kLateRows = HG_LMHEAD_LATE_ROWS;
+
 template <int NT, bool ONE_RANK>
-hipError_t launch_lmhead_n320b_one(const u32x4 *x, const ShardTableN<NT> &wt,
-                                   const OutTableN<NT> &ot, bool keep, bool push,
-                                   const ParityArg &box, int m, int hidden, int shard, int vocab,
-                                   hipStream_t s) {
+hipError_t launch_lmhead_one(const u32x4 *x, const ShardTableN<NT> &wt, const OutTableN<NT> &ot,
+                             bool keep, bool push, const ParityArg &box, int m, int hidden,
+                             int shard, int vocab, hipStream_t s) {
   const dim3 grid((vocab + 319) / 320, (m + kTM - 1) / kTM);
-  if (push && keep)
-    hipLaunchKernelGGL((k_lmhead_n320b<NT, ONE_RANK, true, true>), grid, dim3(512), 0, s, x, wt,
-                       ot, box, m, hidden, shard, vocab);
-  else if (push)
-    hipLaunchKernelGGL((k_lmhead_n320b<NT, ONE_RANK, true, false>), grid, dim3(512), 0, s, x, wt,
-                       ot, box, m, hidden, shard, vocab);
+  auto go = [&](auto late) {
+    constexpr bool L = decltype(late)::value;
+    if (push && keep)
+      hipLaunchKernelGGL((k_lmhead<NT, ONE_RANK, true, true, kStages, L>), grid, dim3(512), 0, s,
+                         x, wt, ot, box, m, hidden, shard, vocab);
+    else if (push)
+      hipLaunchKernelGGL((k_lmhead<NT, ONE_RANK, true, false, kStages, L>), grid, dim3(512), 0, s,
+                         x, wt, ot, box, m, hidden, shard, vocab);
+    else
+      hipLaunchKernelGGL((k_lmhead<NT, ONE_RANK, false, true, kStages, L>), grid, dim3(512), 0, s,
+                         x, wt, ot, box, m, hidden, shard, vocab);
+  };
+  // the late load placement pays once most of a 256-row tile computes
+  if (m >= kLateRows)
+    go(std::integral_constant<bool, true>{});
   else
-    hipLaunchKernelGGL((k_lmhead_n320b<NT, ONE_RANK, false, true>), grid, dim3(512), 0, s, x, wt,
-                       ot, box, m, hidden, shard, vocab);
+    go(std::integral_constant<bool, false>{});
   return hipGetLastError();
 }
 
 template <int NT>
-hipError_t launch_lmhead_n320b_nt(const u32x4 *x, const ShardTable &w, const OutTable &so,
-                                  bool keep, bool push, const ParityArg &box, int m, int hidden,
-                                  int shard, int tp, hipStream_t s) {
+hipError_t launch_lmhead_nt(const u32x4 *x, const ShardTable &w, const OutTable &so, bool keep,
+                            bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
+                            hipStream_t s) {
   ShardTableN<NT> wt;
   OutTableN<NT> ot;
   for (int r = 0; r < NT; ++r) {
@@ -297,12 +389,9 @@ hipError_t launch_lmhead_n320b_nt(const u32x4 *x, const ShardTable &w, const Out
   }
   const int vocab = tp * shard;
   if (shard % 320 == 0)
-    return launch_lmhead_n320b_one<NT, true>(x, wt, ot, keep, push, box, m, hidden, shard, vocab,
-                                             s);
-  return launch_lmhead_n320b_one<NT, false>(x, wt, ot, keep, push, box, m, hidden, shard, vocab,
-                                            s);
+    return launch_lmhead_one<NT, true>(x, wt, ot, keep, push, box, m, hidden, shard, vocab, s);
+  return launch_lmhead_one<NT, false>(x, wt, ot, keep, push, box, m, hidden, shard, vocab, s);
 }
-
 
 }  // namespace
 
@@ -310,10 +399,9 @@ hipError_t launch_lmhead(const u32x4 *x, const ShardTable &w, const OutTable &sh
                          bool push, const ParityArg &box, int m, int hidden, int shard, int tp,
                          hipStream_t s) {
   if (tp <= kSmallTable)
-    return launch_lmhead_n320b_nt<kSmallTable>(x, w, shards_out, keep, push, box, m, hidden, shard,
-                                               tp, s);
-  return launch_lmhead_n320b_nt<HG_MAX_TP>(x, w, shards_out, keep, push, box, m, hidden, shard, tp,
-                                           s);
+    return launch_lmhead_nt<kSmallTable>(x, w, shards_out, keep, push, box, m, hidden, shard, tp,
+                                         s);
+  return launch_lmhead_nt<HG_MAX_TP>(x, w, shards_out, keep, push, box, m, hidden, shard, tp, s);
 }
 
 }  // namespace hg
