@@ -106,3 +106,15 @@ def test_sq_report_derivations(tmp_path):
     assert "L2 hit rate: 75.0 %" in text
     for cmd in ("cmd a", "cmd b", "cmd c"):
         assert "    " + cmd in text
+
+
+def test_m1_fused_times_takes_the_most_frequent_fused_shape(tmp_path):
+    # the timed M=1 loop is the most frequent fused launch; other fused shapes
+    # and other kernels do not enter its median
+    d = ([(FUSED1, 20480, 3000 + 10 * (i % 7)) for i in range(51)] + [(FUSED1, 81920, 3900)] * 20
+         + [(FUSED2, 262144, 61000)] * 30 + [(GEMM, 262144, 650000)] * 60)
+    m1 = profiling.m1_fused_times(_trace(tmp_path, d))
+    assert m1["grid_threads"] == 20480 and m1["calls"] == 51
+    assert m1["median_us"] == 3.03 and m1["min_us"] == 3.0
+    assert m1["kernel_source_sha256_16"] == profiling.kernel_source_hash()
+    assert profiling.m1_fused_times(_trace(tmp_path, [(GEMM, 262144, 650000)])) is None

@@ -91,11 +91,11 @@ struct OutRows {
 // In a launch that completes a call (one-dimensional grid of G workgroups of
 // W waves, N = G*W at most kParitySlots), wave i = b*W + w owns the slots
 // i*K .. i*K + K - 1 with K = kParitySlots / N (the last wave also the
-// remainder): it reads slot i*K and, at its end, writes the other parity into
-// all of its slots -- a contiguous run, so a few cache lines per wave. Every
-// slot is written by exactly one wave, and the only slot a wave of that launch
-// reads is one it rewrites itself after using what it read; no wave waits on
-// another. A launch that only reads the parity may read any slot.
+// remainder): it reads slot i*K and then writes the other parity into all of
+// its slots -- a contiguous run, so a few cache lines per wave. Every slot is
+// written by exactly one wave, and the only slot a wave of that launch reads
+// is one it rewrites itself after reading it; no wave waits on another. A
+// launch that only reads the parity may read any slot.
 constexpr int kParitySlots = 16384;
 
 // Which mailbox parity a launch uses. Host mode (`dev` null): parity `p`,

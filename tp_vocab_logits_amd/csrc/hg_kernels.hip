@@ -293,14 +293,14 @@ __device__ __forceinline__ void collect_chunk(const Geometry &g, int c, int lane
 
 // A launch that completes a call (one-dimensional grid, at most kParitySlots
 // waves) hands the other parity to the next launch in device mode, wave by
-// wave: take_parity reads the wave's first slot, and pass_parity, at the
-// wave's end, writes the other parity into the wave's slots (see
-// kParitySlots). The next
-// launch on the stream, the only other reader, starts after this one has
-// ended, so relaxed stores suffice and nothing waits on them. The value to
-// store and the lane's first slot address are put in vector registers at the
-// start, so the final stores need not wait for earlier stores to release the
-// registers holding their data.
+// wave: take_parity reads the wave's first slot, and pass_parity writes the
+// other parity into the wave's slots (see kParitySlots). No other wave of the
+// launch reads those slots, so a wave writes them as soon as it has read its
+// own, early in the kernel, where the stores overlap the rest of its work
+// (at the wave's end they added a store round trip to every M=1 call: about
+// 0.3 us per gather under graph replay). The next launch on the stream, the
+// only other reader, starts after this one has ended, so relaxed stores
+// suffice and nothing waits on them.
 struct NextParity {
   int p;      // this launch's parity
   int next;   // p ^ 1, held in a vector register
@@ -396,6 +396,7 @@ __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, 
   const NextParity np = take_parity(pa);
   const Box box = make_box(pa.box + np.p * pa.stride, box_bytes);
   if (first) store_chunk<VPT, PUSH>(L0, box);
+  pass_parity(pa, np);
 
   for (int t = me + grid; t < tiles; t += grid) {
     const int c = t * waves + wave;
@@ -409,7 +410,6 @@ __global__ __launch_bounds__(1024) void k_fused(ShardTableN<NT> sh, Geometry g, 
     const int c = t * waves + wave;
     if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud);
   }
-  pass_parity(pa, np);
 }
 
 // Split variant, first half: the push alone, by the ranks whose bit is set in
@@ -438,6 +438,7 @@ __global__ __launch_bounds__(1024) void k_collect(Geometry g, ParityArg pa, unsi
                                                   OutRows out, unsigned *status,
                                                   unsigned long long limit) {
   const NextParity np = take_parity(pa);
+  pass_parity(pa, np);
   u32x4 *box_ptr = pa.box + np.p * pa.stride;
   const int waves = waves_per_block();
   const int wave = wave_id();
@@ -449,7 +450,6 @@ __global__ __launch_bounds__(1024) void k_collect(Geometry g, ParityArg pa, unsi
     const int c = t * waves + wave;
     if (c < g.chunks) collect_chunk<VPT, POLL>(g, c, lane, box, out, status, bud);
   }
-  pass_parity(pa, np);
 }
 
 __global__ __launch_bounds__(256) void k_set_slots(int *slots, int value) {

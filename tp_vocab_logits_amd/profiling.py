@@ -69,6 +69,25 @@ def _stats(ns: list[float]) -> str:
             f"{min(ns) / 1e3:.3f} | {max(ns) / 1e3:.3f}")
 
 
+def m1_fused_times(trace_csv: str) -> dict | None:
+    """Median duration of the M=1 decode fused gather in a kernel trace: the
+    most frequent fused launch shape (the timed loop of bench.py)."""
+    groups: dict[tuple[str, int], list[float]] = {}
+    for name, grid, ns in _dispatches(trace_csv):
+        n = short_name(name)
+        if n.startswith("hg::k_fused<"):
+            groups.setdefault((n, grid), []).append(ns)
+    if not groups:
+        return None
+    key = max(groups, key=lambda k: len(groups[k]))
+    ns = groups[key]
+    return {"kernel": key[0], "grid_threads": key[1], "calls": len(ns),
+            "median_us": round(statistics.median(ns) / 1e3, 3),
+            "mean_us": round(statistics.mean(ns) / 1e3, 3),
+            "min_us": round(min(ns) / 1e3, 3),
+            "kernel_source_sha256_16": kernel_source_hash()}
+
+
 def kernels_report(stats_csv: str, command: str, trace_csv: str | None = None) -> str:
     rows = list(csv.DictReader(open(stats_csv)))
     disp = _dispatches(trace_csv)
@@ -226,6 +245,8 @@ def main() -> None:
     k.add_argument("--command", required=True)
     k.add_argument("--out", required=True)
     k.add_argument("--trace", help="the run's *_kernel_trace.csv, for median durations")
+    k.add_argument("--json", help="also write the M=1 fused gather's median duration (with the "
+                                  "kernel source hash) to this JSON file; needs --trace")
     c = sub.add_parser("counters")
     c.add_argument("fetch_csv")
     c.add_argument("write_csv")
@@ -246,6 +267,13 @@ def main() -> None:
         text = kernels_report(a.stats_csv, a.command, a.trace)
         open(a.out, "w").write(text)
         print(text)
+        if a.json:
+            m1 = m1_fused_times(a.trace)
+            if m1 is None:
+                raise SystemExit("no fused gather in the trace")
+            m1["command"] = a.command
+            open(a.json, "w").write(json.dumps(m1, indent=1) + "\n")
+            print(json.dumps(m1))
     else:
         rep = counters_report(a.fetch_csv, a.write_csv, a.command_fetch, a.command_write)
         open(a.out, "w").write(json.dumps(rep, indent=1) + "\n")
