@@ -224,3 +224,41 @@ def test_producer_epilogue_rewrites_a_sentinel_product():
     assert status == og.OK and np.array_equal(got, want)
     assert hg.poll_status() == _lib.HG_OK
     hg.close()
+
+
+def test_producer_gather_refuses_overlaps():
+    """hg_gemm_gather refuses (HG_EINVAL, nothing enqueued, parity unchanged)
+    a shard copy overlapping the mailbox or the output, an output overlapping
+    a weight block, and hidden states overlapping the mailbox."""
+    import ctypes
+
+    tp, shard, hidden, cap, m = 2, 64, 72, 4, 3
+    note("producer+gather overlap checks")
+    lib = _lib.lib()
+    hg = HeadGather(tp, shard, cap, device=DEV)
+    x = dev(rand_bits((m, hidden), 0.5, 1))
+    w = dev(rand_bits((tp, shard, hidden), 0.5, 2))
+    out = torch.empty((m, tp * shard), dtype=torch.bfloat16, device=DEV)
+    kept = torch.empty((tp, m, shard), dtype=torch.bfloat16, device=DEV)
+    box, nbytes = ctypes.c_void_p(), ctypes.c_size_t()
+    assert lib.hg_mailbox(hg.handle, 0, ctypes.byref(box), ctypes.byref(nbytes)) == _lib.HG_OK
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = _lib.pointer_array
+    wp = P([w[r].data_ptr() for r in range(tp)])
+    kp = [kept[r].data_ptr() for r in range(tp)]
+
+    def call(xp, outp, keep):
+        return lib.hg_gemm_gather(hg.handle, ctypes.c_void_p(xp), wp, hidden, m, ctypes.c_void_p(outp),
+                                  keep, stream)
+
+    assert call(x.data_ptr(), out.data_ptr(), P([box.value, kp[1]])) == _lib.HG_EINVAL  # copy on mailbox
+    assert call(x.data_ptr(), out.data_ptr(), P([kp[0], out.data_ptr()])) == _lib.HG_EINVAL  # copy on out
+    assert call(x.data_ptr(), w[1].data_ptr(), P(kp)) == _lib.HG_EINVAL  # out on a weight block
+    assert call(box.value, out.data_ptr(), P(kp)) == _lib.HG_EINVAL  # x on the mailbox
+    assert hg.parity == 0
+    # and the well-formed call still runs and is served
+    assert call(x.data_ptr(), out.data_ptr(), P(kp)) == _lib.HG_OK
+    sim = og.MailboxSim(tp, shard, cap)
+    status, want = sim.gather(list(bits(kept)))
+    assert status == og.OK and np.array_equal(bits(out), want) and hg.parity == 1
+    hg.close()
