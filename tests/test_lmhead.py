@@ -96,6 +96,20 @@ def test_ragged_sizes_against_oracle(tp, shard, hidden, m):
         assert_close_to_oracle(out[r], x, w[r])
 
 
+@pytest.mark.parametrize("tp,shard,hidden", [(3, 96, 200), (2, 320, 7168)])
+def test_rows_do_not_depend_on_row_count(tp, shard, hidden):
+    """Below 128 rows one wave layout computes the product, from 128 rows on
+    another; both run each 32 x 32 output block as the same chain of MFMAs
+    over K, so a row's bits must not depend on how many rows the call has."""
+    note(f"lmhead rows vs row count tp={tp} shard={shard} hidden={hidden}")
+    x = dev(rand_bits((256, hidden), 0.5, 91))
+    w = dev(rand_bits((tp, shard, hidden), 0.5, 92))
+    full = lmhead(x, w, tp, shard)
+    for m in (1, 5, 127, 128, 200):
+        part = lmhead(x[:m].contiguous(), w, tp, shard)
+        assert torch.equal(part.view(torch.int16), full[:, :m].view(torch.int16)), m
+
+
 def test_lmhead_argument_rules():
     note("lmhead argument rules")
     x = dev(rand_bits((4, 64), 1.0, 3))
@@ -167,12 +181,12 @@ def test_producer_gather_declines_and_state():
     hg.close()
 
 
-@pytest.mark.parametrize("m", [1, 5, 40])
+@pytest.mark.parametrize("m", [1, 5, 40, 130])
 def test_producer_gather_repeated_calls(m):
     # hg_gemm_gather five times in a row: the shards it keeps equal the
     # standalone product's bit for bit, the gather of them is bit-exact to the
     # oracle's, and the parity alternates
-    tp, shard, hidden, cap = 3, 96, 136, 64
+    tp, shard, hidden, cap = 3, 96, 136, 160
     note(f"producer repeated calls m={m}")
     x = dev(rand_bits((m, hidden), 0.5, 70 + m))
     w = dev(rand_bits((tp, shard, hidden), 0.5, 80 + m))
