@@ -12,7 +12,7 @@ from tp_vocab_logits_amd import profiling
 
 FUSED1 = "void hg::(anonymous namespace)::k_fused<1, 2, 2, 8>(hg::Geometry, int)"
 FUSED2 = "void hg::(anonymous namespace)::k_fused<2, 2, 2, 8>(hg::Geometry, int)"
-GEMM = "void hg::(anonymous namespace)::k_lmhead_n320<8, 64, 2, false, true>(int)"
+GEMM = "void hg::(anonymous namespace)::k_lmhead_4x2<8, true, false, true>(int)"
 
 
 def _write(path, header, rows):
