@@ -22,7 +22,8 @@ variant (push, then collect).
 
 Modes: default (the JSON line); ``--pmc-probe`` runs only a plain 256 MiB copy
 and the M=256 fused gather a few times, for ``rocprofv3 --pmc`` counter runs;
-``--gemm-probe`` runs only the M=256 lm_head product three times, likewise;
+``--gemm-probe`` runs only the M=256 lm_head product (``--gemm-probe-calls`` times, 3 by
+default), likewise;
 ``--graph-only`` runs only the graph-replay leg (checked against the oracle),
 for a kernel trace of it.
 """
@@ -72,7 +73,9 @@ def parse_args():
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--pmc-probe", action="store_true")
     ap.add_argument("--gemm-probe", action="store_true",
-                    help="run only the M=256 lm_head product (default implementation) three times")
+                    help="run only the M=256 lm_head product, --gemm-probe-calls times back to back")
+    ap.add_argument("--gemm-probe-calls", type=int, default=3,
+                    help="products the --gemm-probe run launches")
     ap.add_argument("--no-graph", dest="graph", action="store_false",
                     help="skip the graph-replay leg of the M=1 decode gather")
     ap.add_argument("--graph-only", action="store_true",
@@ -149,13 +152,13 @@ def main() -> int:
         sg = torch.empty((wl.tp, wl.rows, wl.shard), dtype=torch.bfloat16, device=dev)
         wptrs = _lib.pointer_array([wg[r].data_ptr() for r in range(wl.tp)])
         sptrs = _lib.pointer_array([sg[r].data_ptr() for r in range(wl.tp)])
-        for _ in range(3):
+        for _ in range(args.gemm_probe_calls):
             rc = lib.hg_lmhead(wl.tp, wl.shard, ctypes.c_void_p(xg.data_ptr()), wptrs, wl.hidden,
                                wl.rows, sptrs, sh)
             if rc:
                 raise _lib.HgError(rc, "hg_lmhead")
         torch.cuda.synchronize()
-        log("gemm probe done: 3 x lm_head X[256,7168] @ W[163840,7168]^T")
+        log(f"gemm probe done: {args.gemm_probe_calls} x lm_head X[256,7168] @ W[163840,7168]^T")
         return 0
 
     # ---------------- M=256 inputs (three rotation sets) --------------------

@@ -118,3 +118,24 @@ def test_m1_fused_times_takes_the_most_frequent_fused_shape(tmp_path):
     assert m1["median_us"] == 3.03 and m1["min_us"] == 3.0
     assert m1["kernel_source_sha256_16"] == profiling.kernel_source_hash()
     assert profiling.m1_fused_times(_trace(tmp_path, [(GEMM, 262144, 650000)])) is None
+
+
+def test_clock_report_per_dispatch(tmp_path):
+    # two dispatches: 500 us at 2.0 GHz with MFMA busy 60 %, 625 us at 1.6 GHz
+    rows, t = [], 10_000
+    for disp, (ns, ghz, busy) in enumerate([(500_000, 2.0, 0.6), (625_000, 1.6, 0.65)]):
+        cyc = ghz * ns
+        for counter, v in (("GRBM_GUI_ACTIVE", 8 * cyc), ("SQ_VALU_MFMA_BUSY_CYCLES", busy * 1024 * cyc)):
+            rows.append([1, disp + 1, "Agent 1", 1, 1, 1, 262144, 3, GEMM, 512, 0, 0, 240, 0, 30, counter, v,
+                         t, t + ns])
+        t += ns + 1000
+    path = tmp_path / "clk_counter_collection.csv"
+    _write(path, ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+                  "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size",
+                  "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value",
+                  "Start_Timestamp", "End_Timestamp"], rows)
+    text = profiling.clock_report(str(path), "k_lmhead", "the command")
+    assert "| 1 | 500.0 | 2.00 | 60.0 | 1000 |" in text
+    assert "| 2 | 625.0 | 1.60 | 65.0 | 1000 |" in text
+    assert "fastest 500.0 us at 2.00 GHz, slowest 625.0 us at 1.60 GHz" in text
+    assert "    the command" in text

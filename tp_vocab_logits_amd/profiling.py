@@ -21,6 +21,14 @@ Usage::
         --command-fetch CMD --command-write CMD --out FILE.json
     python -m tp_vocab_logits_amd.profiling sq CSV [CSV ...] --kernel NAME \\
         --command CMD [--command CMD ...] --out FILE.md
+    python -m tp_vocab_logits_amd.profiling clock CSV --kernel NAME --command CMD --out FILE.md
+
+``sq`` -- median SQ/TCC/GRBM counters of a kernel over several ``--pmc`` runs,
+    with the shader clock, MFMA busy fraction and waits derived from them.
+
+``clock`` -- one ``--pmc GRBM_GUI_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES`` run over
+    many back-to-back dispatches of a kernel: each dispatch's duration, shader
+    clock and MFMA busy fraction, in launch order.
 """
 
 from __future__ import annotations
@@ -237,6 +245,46 @@ def sq_report(csvs: list[str], kernel: str, commands: list[str]) -> str:
     return "\n".join(lines) + "\n"
 
 
+def clock_report(csv_path: str, kernel: str, command: str) -> str:
+    """Per-dispatch duration, shader clock (GRBM_GUI_ACTIVE / 8 XCDs over the
+    dispatch's duration) and MFMA busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over
+    1024 SIMDs' cycles) of the kernels whose name contains ``kernel``."""
+    per: dict[int, dict[str, float]] = {}
+    names: set[str] = set()
+    for r in csv.DictReader(open(csv_path)):
+        if kernel not in r["Kernel_Name"]:
+            continue
+        names.add(short_name(r["Kernel_Name"]))
+        d = per.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    rows = []
+    for disp in sorted(per):
+        d = per[disp]
+        if "GRBM_GUI_ACTIVE" not in d:
+            continue
+        cyc = d["GRBM_GUI_ACTIVE"] / XCDS
+        busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * cyc) if "SQ_VALU_MFMA_BUSY_CYCLES" in d else None
+        rows.append((disp, d["ns"] / 1e3, cyc / d["ns"], busy))
+    lines = ["# Shader clock under back-to-back lm_head products (rocprofv3)", "",
+             "Kernel " + ", ".join(f"`{n}`" for n in sorted(names)) + ".", "",
+             "Command (TMPDIR=/tmp; paths relative to the repository root):", "", "    " + command, "",
+             "| launch | duration us | shader clock GHz | MFMA busy % | duration x clock (k cycles) |",
+             "|---|---|---|---|---|"]
+    for n, (disp, us, ghz, busy) in enumerate(rows):
+        b = f"{busy * 100:.1f}" if busy is not None else "-"
+        lines.append(f"| {n + 1} | {us:.1f} | {ghz:.2f} | {b} | {us * ghz:.0f} |")
+    if rows:
+        us = [r[1] for r in rows]
+        ghz = [r[2] for r in rows]
+        fast = min(range(len(rows)), key=lambda i: us[i])
+        slow = max(range(len(rows)), key=lambda i: us[i])
+        lines += ["", f"{len(rows)} dispatches: fastest {us[fast]:.1f} us at {ghz[fast]:.2f} GHz, "
+                      f"slowest {us[slow]:.1f} us at {ghz[slow]:.2f} GHz, median "
+                      f"{statistics.median(us):.1f} us at {statistics.median(ghz):.2f} GHz."]
+    return "\n".join(lines) + "\n"
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -258,8 +306,17 @@ def main() -> None:
     q.add_argument("--kernel", required=True, help="substring of the kernel name")
     q.add_argument("--command", action="append", required=True)
     q.add_argument("--out", required=True)
+    w = sub.add_parser("clock")
+    w.add_argument("csv", help="*_counter_collection.csv of the --pmc run")
+    w.add_argument("--kernel", required=True, help="substring of the kernel name")
+    w.add_argument("--command", required=True)
+    w.add_argument("--out", required=True)
     a = ap.parse_args()
-    if a.what == "sq":
+    if a.what == "clock":
+        text = clock_report(a.csv, a.kernel, a.command)
+        open(a.out, "w").write(text)
+        print(text)
+    elif a.what == "sq":
         text = sq_report(a.csvs, a.kernel, a.command)
         open(a.out, "w").write(text)
         print(text)
