@@ -496,7 +496,7 @@ __global__ __launch_bounds__(1024) void k_stock(ShardTableN<NT> sh, Geometry g, 
 // The stock concatenation for rows that are not a whole number of 16-byte
 // vectors: one 2-byte element per lane and step, out[i][j] for j < cols.
 template <int NT>
-__global__ __launch_bounds__(256) void k_stock_elem(ShardTableN<NT> sh, int tp, int shard, int m,
+__global__ __launch_bounds__(256) void k_stock_elem(ShardTableN<NT> sh, int shard, int m,
                                                     unsigned short *out, int cols) {
   const long long n = static_cast<long long>(m) * cols;
   const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
@@ -644,7 +644,7 @@ hipError_t launch_stock_elem(const ShardTable &sh, int tp, int shard, int m, uns
                              int cols, int grid, int block, hipStream_t s) {
   return by_table(sh, tp, [&](const auto &t) {
     constexpr int NT = sizeof(t.p) / sizeof(t.p[0]);
-    hipLaunchKernelGGL((k_stock_elem<NT>), dim3(grid), dim3(block), 0, s, t, tp, shard, m, out,
+    hipLaunchKernelGGL((k_stock_elem<NT>), dim3(grid), dim3(block), 0, s, t, shard, m, out,
                        cols);
     return hipGetLastError();
   });
