@@ -652,8 +652,13 @@ def main() -> int:
                      "kernel": "k_fused (M=256 gather, cold)" if args.variant == "fused"
                                else "k_push + k_collect (M=256 gather, cold)"},
         "m1_kernel_time_rocprof": None if not m1_rocprof else {
-            leg: {"median_us": t["median_us"], "calls": t["calls"], "kernel": t["kernel"],
-                  "trace": os.path.relpath(M1_TRACES[leg], ROOT)} for leg, t in m1_rocprof.items()},
+            **{leg: {"median_us": t["median_us"], "calls": t["calls"], "kernel": t["kernel"],
+                     "trace": os.path.relpath(M1_TRACES[leg], ROOT)} for leg, t in m1_rocprof.items()},
+            **({"split_eager": {"push_median_us": m1_rocprof["eager"]["split"]["push"]["median_us"],
+                                "collect_median_us": m1_rocprof["eager"]["split"]["collect"]["median_us"],
+                                "sum_median_us": m1_rocprof["eager"]["split"]["sum_median_us"],
+                                "trace": os.path.relpath(M1_TRACES["eager"], ROOT)}}
+               if "split" in m1_rocprof.get("eager", {}) else {})},
         "roofline_m1": {"bound": "latency",
                         "achieved": round(dec_bytes / (m1_basis_us * 1e-6) / 1e9, 1),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",

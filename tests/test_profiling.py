@@ -139,3 +139,14 @@ def test_clock_report_per_dispatch(tmp_path):
     assert "| 2 | 625.0 | 1.60 | 65.0 | 1000 |" in text
     assert "fastest 500.0 us at 2.00 GHz, slowest 625.0 us at 1.60 GHz" in text
     assert "    the command" in text
+
+
+def test_m1_split_times_sum_push_and_collect_at_the_decode_grid(tmp_path):
+    push = "void hg::(anonymous namespace)::k_push<1, 8>(int)"
+    coll = "void hg::(anonymous namespace)::k_collect<1, 1>(int)"
+    d = ([(push, 20480, 2700 + 10 * (i % 3)) for i in range(30)] + [(coll, 20480, 2800)] * 30
+         + [(push, 1048576, 30000)] * 40 + [(coll, 1048576, 37000)] * 40)
+    sp = profiling.m1_split_times(_trace(tmp_path, d), 20480)
+    assert sp["push"]["median_us"] == 2.71 and sp["collect"]["median_us"] == 2.8
+    assert sp["sum_median_us"] == 5.51 and sp["push"]["calls"] == 30
+    assert profiling.m1_split_times(_trace(tmp_path, [(push, 20480, 2700)]), 20480) is None

@@ -96,6 +96,27 @@ def m1_fused_times(trace_csv: str) -> dict | None:
             "kernel_source_sha256_16": kernel_source_hash()}
 
 
+def m1_split_times(trace_csv: str, grid_threads: int) -> dict | None:
+    """Medians of the split variant's two launches (``k_push``, ``k_collect``)
+    at the M=1 fused gather's grid, and their sum: the split M=1 gather's
+    kernel time."""
+    groups: dict[str, dict[str, list[float]]] = {"push": {}, "collect": {}}
+    for name, grid, ns in _dispatches(trace_csv):
+        n = short_name(name)
+        for part, prefix in (("push", "hg::k_push<"), ("collect", "hg::k_collect<")):
+            if n.startswith(prefix) and grid == grid_threads:
+                groups[part].setdefault(n, []).append(ns)
+    out: dict = {}
+    for part, g in groups.items():
+        if not g:
+            return None
+        k = max(g, key=lambda n: len(g[n]))
+        out[part] = {"kernel": k, "calls": len(g[k]),
+                     "median_us": round(statistics.median(g[k]) / 1e3, 3)}
+    out["sum_median_us"] = round(out["push"]["median_us"] + out["collect"]["median_us"], 3)
+    return out
+
+
 def kernels_report(stats_csv: str, command: str, trace_csv: str | None = None) -> str:
     rows = list(csv.DictReader(open(stats_csv)))
     disp = _dispatches(trace_csv)
@@ -328,6 +349,9 @@ def main() -> None:
             m1 = m1_fused_times(a.trace)
             if m1 is None:
                 raise SystemExit("no fused gather in the trace")
+            split = m1_split_times(a.trace, m1["grid_threads"])
+            if split is not None:
+                m1["split"] = split
             m1["command"] = a.command
             open(a.json, "w").write(json.dumps(m1, indent=1) + "\n")
             print(json.dumps(m1))
