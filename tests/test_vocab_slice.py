@@ -138,10 +138,13 @@ def test_declined_calls_return_the_sliced_stock_gather():
     assert hg.parity == 0
 
 
-def test_producer_gather_slices():
-    tp, shard, cap, m, hidden = 2, 256, 4, 3, 64
+@pytest.mark.parametrize("m", [3, 130])
+def test_producer_gather_slices(m):
+    # 3 rows: the 8 x 1 product; 130 rows: the 4 x 2 product's epilogue push
+    tp, shard, hidden = 2, 256, 64
+    cap = m + 1
     for vocab in (505, 496, 2 * shard):
-        note(f"producer + gather vocab={vocab}")
+        note(f"producer + gather m={m} vocab={vocab}")
         hg, sim = HeadGather(tp, shard, cap, device=DEV, vocab=vocab), og.MailboxSim(tp, shard, cap)
         hg.set_poll_limit(1 << 20)
         x = dev(syn.random_bf16((m, hidden), 0.5, vocab))
