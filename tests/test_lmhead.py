@@ -181,12 +181,12 @@ def test_producer_gather_declines_and_state():
     hg.close()
 
 
-@pytest.mark.parametrize("m", [1, 5, 40, 130])
+@pytest.mark.parametrize("m", [1, 5, 40, 130, 300])
 def test_producer_gather_repeated_calls(m):
     # hg_gemm_gather five times in a row: the shards it keeps equal the
     # standalone product's bit for bit, the gather of them is bit-exact to the
     # oracle's, and the parity alternates
-    tp, shard, hidden, cap = 3, 96, 136, 160
+    tp, shard, hidden, cap = 3, 96, 136, 320
     note(f"producer repeated calls m={m}")
     x = dev(rand_bits((m, hidden), 0.5, 70 + m))
     w = dev(rand_bits((tp, shard, hidden), 0.5, 80 + m))
