@@ -6,7 +6,8 @@
  *
  * usage: hg_client IN OUT
  * IN:  int32 tp, shard, cap, m, calls, variant (0: hg_gather, 1: hg_push +
- *      hg_collect), then `calls` input sets of tp x m x shard BF16 (uint16).
+ *      hg_collect, 2: hg_gather_static, which leaves the context untouched),
+ *      then `calls` input sets of tp x m x shard BF16 (uint16).
  * OUT: per call m x tp*shard BF16 outputs; then int32 parity; then both
  *      mailbox parities, cap x tp*shard BF16 each.
  * Exit status 0 on success; otherwise the failing step goes to stderr.
@@ -81,6 +82,9 @@ int main(int argc, char **argv) {
     if (variant == 0) {
       rc = hg_gather(h, (const void *const *)dev_shards, m, dev_out, s);
       if (rc != HG_OK) return fail("hg_gather", rc);
+    } else if (variant == 2) {
+      rc = hg_gather_static(tp, shard, (const void *const *)dev_shards, m, dev_out, s);
+      if (rc != HG_OK) return fail("hg_gather_static", rc);
     } else {
       rc = hg_push(h, (const void *const *)dev_shards, m, s);
       if (rc != HG_OK) return fail("hg_push", rc);

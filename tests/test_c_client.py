@@ -1,7 +1,8 @@
 """GPU: the C ABI from a plain C program (tests/c_client/hg_client.c: no
 Python, no torch, only include/hg.h and the HIP runtime), checked against the
 CPU oracle's protocol simulator: every output, the final parity and both
-mailbox parities, bit for bit, fused and split."""
+mailbox parities, bit for bit, fused and split; and the allocation-free
+hg_gather_static against the oracle's definition."""
 
 from __future__ import annotations
 
@@ -29,12 +30,14 @@ def note(msg: str) -> None:
     ("spec", 8, 20480, 8, 4, 3, 1),
     ("spec", 3, 288, 4, 3, 5, 0),
     ("batched", 5, 40, 6, 6, 4, 1),
+    ("decode", 8, 20480, 8, 1, 3, 2),
+    ("spec", 3, 288, 4, 3, 4, 2),
 ])
 def test_c_client_against_oracle(tmp_path, workload, tp, shard, cap, m, calls, variant):
     if not os.path.exists(CLIENT):
         pytest.fail("tests/c_client/hg_client is missing: run __graft_entry__.build() first")
     note(f"C client {workload} tp={tp} shard={shard} cap={cap} m={m} calls={calls} "
-         f"{'split' if variant else 'fused'}")
+         f"{['fused', 'split', 'static'][variant]}")
     sets = []
     for k in range(calls):
         s = syn.shard_set(workload, k, rows=m, tp=tp, shard=shard)
@@ -57,6 +60,8 @@ def test_c_client_against_oracle(tmp_path, workload, tp, shard, cap, m, calls, v
         off += n
         if variant == 0:
             status, want = sim.gather(list(s))
+        elif variant == 2:  # the static entry point: the context stays as created
+            status, want = og.OK, og.gather_definition(list(s))
         else:
             assert sim.push(list(s)) == og.OK
             status, want = sim.collect(m)
