@@ -136,9 +136,13 @@ def test_graph_of_split_push_collect():
     assert hg.poll_status() == _lib.HG_OK
 
 
-def test_graph_of_producer_gather():
-    tp, shard, cap, m, hidden = 2, 256, 3, 3, 192
-    note("graph of lm_head producer + gather, device parity")
+@pytest.mark.parametrize("m", [3, 130])
+def test_graph_of_producer_gather(m):
+    # 3 rows: the 8 x 1 product; 130: the 4 x 2 product, whose epilogue reads
+    # the device parity too
+    tp, shard, hidden = 2, 256, 192
+    cap = m
+    note(f"graph of lm_head producer + gather, device parity, m={m}")
     hg, sim = make(tp, shard, cap), og.MailboxSim(tp, shard, cap)
     hg.set_device_parity(True)
     x = dev(syn.random_bf16((m, hidden), 0.5, 1))
