@@ -63,6 +63,28 @@ def kernel_source_hash() -> str:
     return h()
 
 
+def current_profiles(paths: dict, counters: str, variant: str, source_hash: str):
+    """The committed profile summaries that still describe the current kernel
+    sources: the M=1 fused gather's kernel times per leg (JSON files of
+    ``paths``, keyed by leg) and the M=256 traffic per launch from the counter
+    summary ``counters`` (for ``variant``). A summary taken on other sources
+    (another hash) is left out; a missing file too."""
+    m1 = {}
+    for leg, path in paths.items():
+        if os.path.exists(path):
+            with open(path) as f:
+                t = json.load(f)
+            if t.get("kernel_source_sha256_16") == source_hash:
+                m1[leg] = t
+    traffic = None
+    if os.path.exists(counters):
+        with open(counters) as f:
+            c = json.load(f)
+        if c.get("kernel_source_sha256_16") == source_hash and c.get("variant") == variant:
+            traffic = c.get("traffic_bytes_per_launch")
+    return m1, traffic
+
+
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -591,23 +613,11 @@ def main() -> int:
                 "rel_frobenius_error_gpu_vs_oracle": err}
 
     # ---------------- counters (only if taken on this kernel source) --------
-    traffic = None
-    if os.path.exists(COUNTERS):
-        with open(COUNTERS) as f:
-            c = json.load(f)
-        if c.get("kernel_source_sha256_16") == kernel_source_hash() and c.get("variant") == args.variant:
-            traffic = c.get("traffic_bytes_per_launch")
+    # rocprof kernel times of the M=1 fused gather and the M=256 traffic, from
+    # the committed summaries, while they were taken on the current sources
+    m1_rocprof, traffic = current_profiles(M1_TRACES, COUNTERS, args.variant, kernel_source_hash())
 
     dec_bytes = 5 * wd.rows * wd.vocab * 2
-    # rocprof kernel times of the M=1 fused gather, from the committed traces
-    # of this benchmark, while they were taken on the current kernel sources
-    m1_rocprof = {}
-    for leg, path in M1_TRACES.items():
-        if os.path.exists(path):
-            with open(path) as f:
-                t = json.load(f)
-            if t.get("kernel_source_sha256_16") == kernel_source_hash():
-                m1_rocprof[leg] = t
     m1_kernel_us = m1_rocprof["eager"]["median_us"] if "eager" in m1_rocprof else None
     m1_basis_us = m1_kernel_us if m1_kernel_us is not None else us_m1
     line = {
